@@ -1,0 +1,84 @@
+"""Oracle: gradients of chunked causal attention from the final LSE (float64).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.
+
+The pages train the 2M-token model without gradient checkpointing ("LongVILA
+- ... (Jason's Study)", section "What it is"; the Chinese news page makes the
+same statement), so the backward consumes the forward's saved output ``O`` and
+log-sum-exp rather than recomputing the layer.  The gradients themselves are
+the plain calculus of the forward definition in :mod:`oracle.attention`,
+evaluated per chunk with the *final* (all-chunk) LSE:
+
+    P_ij  = exp(s_ij - LSE_i)        for visible j, else 0
+    dV_j  = sum_i P_ij dO_i
+    dP_ij = dO_i . v_j
+    D_i   = dO_i . O_i               (O = final merged output)
+    dS_ij = P_ij (dP_ij - D_i)
+    dQ_i  = scale * sum_j dS_ij k_j
+    dK_j  = scale * sum_i dS_ij q_i
+
+For grouped-query attention dK and dV of a KV head are summed over the query
+heads mapped to it (``h // G``).  Summing the per-chunk ``dQ`` over all chunks
+gives the gradient of the full attention.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+_ROWS = 256
+
+
+def bwd_delta(o, do):
+    """``D[h, i] = sum_c dO[i, h, c] * O[i, h, c]`` as ``[Hq, Sq]``."""
+    o = np.asarray(o, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    return np.einsum("ihc,ihc->hi", do, o)
+
+
+def attention_backward(q, k, v, do, lse, delta, q_pos, k_pos, scale=None):
+    """Return ``(dq, dk, dv)`` of one chunk.
+
+    ``q, do``: ``[Sq, Hq, d]``; ``k, v``: ``[Sk, Hkv, d]``; ``lse, delta``:
+    ``[Hq, Sq]`` (final LSE over all chunks, and ``D`` from :func:`bwd_delta`).
+    ``dq`` is this chunk's contribution ``[Sq, Hq, d]``; ``dk, dv`` are
+    ``[Sk, Hkv, d]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    delta = np.asarray(delta, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    sq, hq, d = q.shape
+    sk, hkv, _ = k.shape
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(hq):
+        kv = h // group
+        kh = k[:, kv, :]
+        vh = v[:, kv, :]
+        for b0 in range(0, sq, _ROWS):
+            r = slice(b0, min(b0 + _ROWS, sq))
+            qp = q_pos[r]
+            cols = np.nonzero(k_pos <= qp.max())[0]
+            if cols.size == 0:
+                continue
+            vis = k_pos[cols][None, :] <= qp[:, None]
+            l_r = lse[h, r]
+            live = np.isfinite(l_r)
+            s = (q[r, h, :] @ kh[cols].T) * scale
+            p = np.where(vis & live[:, None],
+                         np.exp(s - np.where(live, l_r, 0.0)[:, None]), 0.0)
+            dv[cols, kv, :] += p.T @ do[r, h, :]
+            dp = do[r, h, :] @ vh[cols].T
+            ds = p * (dp - delta[h, r][:, None])
+            dq[r, h, :] += scale * (ds @ kh[cols])
+            dk[cols, kv, :] += scale * (ds.T @ q[r, h, :])
+    return dq, dk, dv
