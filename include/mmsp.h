@@ -1,0 +1,172 @@
+/*
+ * mmsp.h -- C-ABI of libmmsp.so: one rank's share of multi-modal sequence-
+ * parallel (MM-SP) causal attention on an AMD MI355X (gfx950).
+ *
+ * What is computed (sources are web pages, cited by title and section):
+ *
+ *  - "LongVILA Guide: 2M Context Multi-Modal AI Model", section
+ *    "Multi-Modal Sequence Parallelism (MM-SP) Mechanics": each rank holds
+ *    N/P tokens; K/V chunks travel around a ring and every ring step runs one
+ *    attention kernel of the local queries against the chunk that arrived.
+ *  - Same page, section "Implementation: PyTorch Distributed Pipeline and
+ *    Token Routing": the per-step body scales the query-key dot products by
+ *    1/sqrt(head_dim), applies a softmax and accumulates the weighted values
+ *    into an output accumulator, one chunk per step.
+ *  - Same page, section "Problem", item 2, and "Ultra-Large Multimodal LLM
+ *    Inference ...", section 4 "Load Balancing for Tensor Parallelism":
+ *    modality-dense and text-only regions give ranks unequal work; work is
+ *    dispatched by modality token density.
+ *  - "LongVILA - ... (Jason's Study)", section "What it is": training at 2M
+ *    tokens runs without gradient checkpointing, so the backward consumes
+ *    the saved forward statistics.
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *    keeps no pointer after the call returns and allocates no device memory
+ *    (scratch comes from the caller, sized by a *_workspace_bytes query).
+ *  - bf16 tensors are passed as `const void*` holding IEEE bfloat16 bits.
+ *    Layouts are row-major and contiguous: token-major activations
+ *    [tokens][heads][head_dim]; per-head statistics [heads][tokens].
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; device faults surface at the caller's
+ *    next synchronisation of that stream.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    nonzero return means nothing was launched.  Calls are thread-safe and
+ *    keep no global device state.  Position arrays must be strictly
+ *    increasing (a precondition, not checked).
+ */
+#ifndef MMSP_H
+#define MMSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status ------------------------------------------------------------ */
+enum {
+  MMSP_OK = 0,
+  MMSP_ERR_NULL = -1,         /* a required pointer is NULL                 */
+  MMSP_ERR_SHAPE = -2,        /* a size is <= 0, too large, or scale <= 0   */
+  MMSP_ERR_UNSUPPORTED = -3,  /* head_dim not in {64,128}; unknown mode/flag*/
+  MMSP_ERR_DIVISIBILITY = -4, /* hq % hkv != 0; n not divisible by 2*P*g    */
+  MMSP_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than required    */
+  MMSP_ERR_HIP = -6           /* the HIP runtime reported a launch error    */
+};
+
+/* Static string naming a status code ("unknown status" for others). */
+const char* mmsp_status_string(int status);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int mmsp_abi_version(void);
+#define MMSP_ABI_VERSION 1
+
+/* ---- a1: shard balance ---------------------------------------------------
+ * Permutation of an n-token stream into n_ranks shards of equal causal work
+ * (query position p attends to p+1 keys).  Problem statement: "LongVILA
+ * Guide ...", section "Problem", item 2; remedy by modality token density:
+ * "Ultra-Large Multimodal LLM Inference ...", section 4.
+ *
+ * MMSP_BALANCE_ZIGZAG: requires n % (2*n_ranks) == 0, L = n/(2*n_ranks);
+ *   rank r owns positions [r*L,(r+1)*L) then [(2P-1-r)*L,(2P-r)*L).
+ *   `d_labels` may be NULL; `granularity` is ignored.
+ * MMSP_BALANCE_MODALITY: requires n % (2*n_ranks*granularity) == 0.  Blocks
+ *   of `granularity` tokens; each round of 2P consecutive blocks is paired
+ *   outside-in (pair a = blocks 2jP+a and 2jP+2P-1-a); pairs in order of
+ *   decreasing visual count (ties: smaller a) go to ranks in order of
+ *   increasing running visual total (ties: smaller rank).  `d_labels` is
+ *   uint8[n], 0 = text, nonzero = visual.
+ *
+ * Output: d_perm int32[n], rank-major: rank r's positions are
+ * d_perm[r*n/P .. (r+1)*n/P), ascending.  d_inv_perm (nullable) int32[n]
+ * with d_inv_perm[d_perm[i]] = i.  1 <= n_ranks <= 1024, n <= 2^31-1.
+ * The result is an integer function of the labels: bit-exact and unique.
+ */
+enum { MMSP_BALANCE_ZIGZAG = 0, MMSP_BALANCE_MODALITY = 1 };
+
+size_t mmsp_shard_balance_workspace_bytes(int64_t n, int32_t n_ranks, int32_t mode,
+                                          int32_t granularity);
+int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
+                       int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
+                       void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* ---- a2: attention of the query shard against one KV chunk ---------------
+ * Source: "LongVILA Guide ...", sections "Multi-Modal Sequence Parallelism
+ * (MM-SP) Mechanics" (one attention kernel per ring step on the current KV
+ * chunk) and "Implementation ..." (scores = q.k * scale, softmax, weighted
+ * sum of V).
+ *
+ * q      bf16 [sq][hq][d]          k, v   bf16 [sk][hkv][d]
+ * q_pos  int32 [sq], k_pos int32 [sk]: global token positions, strictly
+ *        increasing; with MMSP_CAUSAL key j is visible to query i iff
+ *        k_pos[j] <= q_pos[i] (may be NULL without MMSP_CAUSAL: all visible).
+ * scale  > 0; the usual value is 1/sqrt(d).
+ * GQA    query head h reads KV head h / (hq/hkv); requires hq % hkv == 0.
+ * o      fp32 [sq][hq][d]; lse fp32 [hq][sq] (natural log of the sum of
+ *        exp(scale*q.k) over the visible keys of this chunk).
+ * flags  MMSP_CAUSAL | MMSP_ACCUMULATE.  Without ACCUMULATE, (o, lse) are
+ *        overwritten with this chunk's normalised result; a row with no
+ *        visible key gets o = 0, lse = -inf.  With ACCUMULATE, (o, lse) hold a
+ *        running result over earlier chunks (start from o = 0, lse = -inf)
+ *        and are merged in place with this chunk's result exactly as
+ *        mmsp_lse_merge does; rows with no visible key are left untouched.
+ * d in {64, 128}; sq, sk >= 1; hq*sq*d and hkv*sk*d < 2^31.
+ */
+enum { MMSP_CAUSAL = 1u, MMSP_ACCUMULATE = 2u };
+
+int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32_t* q_pos,
+                        const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
+                        int32_t d, float scale, uint32_t flags, float* o, float* lse,
+                        void* stream);
+
+/* ---- a3: log-sum-exp merge of two chunk results ---------------------------
+ * The page's ring loop ("Implementation ...") adds each step's output into an
+ * accumulator; the exact form of that accumulation over disjoint key sets is
+ *   L = ln(e^La + e^Lb),  O = e^(La-L) O_a + e^(Lb-L) O_b,
+ * with (0, -inf) as identity and two empty rows giving (0, -inf).
+ *
+ * o_acc fp32 [sq][hq][d], lse_acc fp32 [hq][sq]: updated in place.
+ * o_part, lse_part: the other operand (same layouts); both NULL means "no
+ *   operand": only o_final_bf16 is produced from (o_acc, lse_acc).
+ * o_final_bf16 (nullable): bf16 [sq][hq][d] copy of the merged o
+ *   (round-to-nearest-even).  d in {64, 128}.
+ */
+int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                   int32_t sq, int32_t hq, int32_t d, void* o_final_bf16, void* stream);
+
+/* ---- a5: backward preprocess ----------------------------------------------
+ * delta[h][i] = sum_c dout[i][h][c] * o[i][h][c] (fp32 accumulation) from the
+ * saved final output; o, dout bf16 [sq][hq][d]; delta fp32 [hq][sq].
+ */
+int mmsp_attn_bwd_preprocess(const void* o, const void* dout, int32_t sq, int32_t hq, int32_t d,
+                             float* delta, void* stream);
+
+/* ---- a6: backward of one chunk from the saved final LSE --------------------
+ * Training without gradient checkpointing ("LongVILA - ... (Jason's Study)",
+ * section "What it is"): P = exp(scale*q.k - LSE_final) on visible pairs,
+ *   dV = P^T dO,  dS = P o (dO V^T - delta),  dQ += scale dS K,
+ *   dK = scale dS^T Q,
+ * with dK, dV of a KV head summed over its hq/hkv query heads.
+ *
+ * q, dout bf16 [sq][hq][d]; k, v bf16 [sk][hkv][d]; lse, delta fp32 [hq][sq]
+ * (lse = final merged LSE over all chunks; rows with lse = -inf contribute
+ * nothing); q_pos/k_pos as in mmsp_attn_fwd_chunk.
+ * dq_acc fp32 [sq][hq][d]: this chunk's dQ is ADDED (zero it before the first
+ *   chunk); additions use device atomics, so the summation order -- and the
+ *   last bits of dq_acc -- may differ between runs.
+ * dk, dv fp32 [sk][hkv][d]: overwritten, or added to with MMSP_ACCUMULATE.
+ */
+int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, const float* delta, const int32_t* q_pos,
+                        const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
+                        int32_t d, float scale, uint32_t flags, float* dq_acc, float* dk,
+                        float* dv, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMSP_H */

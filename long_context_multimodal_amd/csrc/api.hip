@@ -1,0 +1,175 @@
+// C-ABI of libmmsp.so (declared and documented in include/mmsp.h).
+//
+// Every entry point validates its arguments on the host and returns a
+// status before anything is enqueued; it never allocates device memory and
+// never synchronises.  Launch errors are reported as MMSP_ERR_HIP.
+#include <math.h>
+
+#include "../../include/mmsp.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr long long kMaxElems = 0x7fffffffLL;  // element offsets stay in int32 range per row
+constexpr int kMaxRanks = 1024;
+
+inline bool bad_dim(int32_t d) { return d != 64 && d != 128; }
+
+inline int check_hip(hipError_t e) { return e == hipSuccess ? MMSP_OK : MMSP_ERR_HIP; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_attn_shapes(int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale) {
+  if (sq <= 0 || sk <= 0 || hq <= 0 || hkv <= 0) return MMSP_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return MMSP_ERR_SHAPE;
+  if (bad_dim(d)) return MMSP_ERR_UNSUPPORTED;
+  if (hq % hkv != 0) return MMSP_ERR_DIVISIBILITY;
+  if ((long long)sq * hq * d > kMaxElems || (long long)sk * hkv * d > kMaxElems)
+    return MMSP_ERR_SHAPE;
+  return MMSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mmsp_status_string(int status) {
+  switch (status) {
+    case MMSP_OK: return "ok";
+    case MMSP_ERR_NULL: return "a required pointer is NULL";
+    case MMSP_ERR_SHAPE: return "invalid size or scale";
+    case MMSP_ERR_UNSUPPORTED: return "unsupported head_dim, mode or flag";
+    case MMSP_ERR_DIVISIBILITY: return "divisibility requirement not met";
+    case MMSP_ERR_WORKSPACE: return "workspace missing or too small";
+    case MMSP_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int mmsp_abi_version(void) { return MMSP_ABI_VERSION; }
+
+size_t mmsp_shard_balance_workspace_bytes(int64_t n, int32_t n_ranks, int32_t mode,
+                                          int32_t granularity) {
+  (void)n_ranks;
+  if (mode != MMSP_BALANCE_MODALITY || n <= 0 || granularity <= 0) return 0;
+  const int64_t n_blocks = n / granularity;
+  return (size_t)(2 * n_blocks) * sizeof(int32_t);
+}
+
+int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
+                       int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
+                       void* d_workspace, size_t workspace_bytes, void* stream) {
+  if (mode != MMSP_BALANCE_ZIGZAG && mode != MMSP_BALANCE_MODALITY) return MMSP_ERR_UNSUPPORTED;
+  if (d_perm == nullptr) return MMSP_ERR_NULL;
+  if (mode == MMSP_BALANCE_MODALITY && d_labels == nullptr) return MMSP_ERR_NULL;
+  if (n <= 0 || n > kMaxElems || n_ranks <= 0 || n_ranks > kMaxRanks) return MMSP_ERR_SHAPE;
+  int32_t* ws_vis = nullptr;
+  int32_t* ws_owner = nullptr;
+  if (mode == MMSP_BALANCE_ZIGZAG) {
+    if (n % (2LL * n_ranks) != 0) return MMSP_ERR_DIVISIBILITY;
+  } else {
+    if (granularity <= 0) return MMSP_ERR_SHAPE;
+    if (n % (2LL * n_ranks * granularity) != 0) return MMSP_ERR_DIVISIBILITY;
+    const size_t need = mmsp_shard_balance_workspace_bytes(n, n_ranks, mode, granularity);
+    if (d_workspace == nullptr || workspace_bytes < need) return MMSP_ERR_WORKSPACE;
+    ws_vis = static_cast<int32_t*>(d_workspace);
+    ws_owner = ws_vis + n / granularity;
+  }
+  return check_hip(mmsp::launch_shard_balance(d_labels, (int)n, n_ranks, mode, granularity,
+                                              d_perm, d_inv_perm, ws_vis, ws_owner,
+                                              as_stream(stream)));
+}
+
+int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32_t* q_pos,
+                        const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
+                        int32_t d, float scale, uint32_t flags, float* o, float* lse,
+                        void* stream) {
+  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
+  const bool causal = (flags & MMSP_CAUSAL) != 0;
+  if (!q || !k || !v || !o || !lse) return MMSP_ERR_NULL;
+  if (causal && (!q_pos || !k_pos)) return MMSP_ERR_NULL;
+  const int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
+  if (st != MMSP_OK) return st;
+  mmsp::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.q_pos = q_pos;
+  p.k_pos = k_pos;
+  p.o = o;
+  p.lse = lse;
+  p.sq = sq;
+  p.sk = sk;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  const int bm = mmsp::fwd_rows_per_block();
+  p.n_qtiles = (sq + bm - 1) / bm;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal ? 1 : 0;
+  p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
+  return check_hip(mmsp::launch_attn_fwd(p, d, as_stream(stream)));
+}
+
+int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                   int32_t sq, int32_t hq, int32_t d, void* o_final_bf16, void* stream) {
+  if (!o_acc || !lse_acc) return MMSP_ERR_NULL;
+  if ((o_part == nullptr) != (lse_part == nullptr)) return MMSP_ERR_NULL;
+  if (sq <= 0 || hq <= 0) return MMSP_ERR_SHAPE;
+  if (bad_dim(d)) return MMSP_ERR_UNSUPPORTED;
+  if ((long long)sq * hq * d > kMaxElems) return MMSP_ERR_SHAPE;
+  if (o_part == nullptr && o_final_bf16 == nullptr) return MMSP_OK;  // nothing to do
+  return check_hip(mmsp::launch_lse_merge(o_acc, lse_acc, o_part, lse_part, sq, hq, d,
+                                          static_cast<uint16_t*>(o_final_bf16),
+                                          as_stream(stream)));
+}
+
+int mmsp_attn_bwd_preprocess(const void* o, const void* dout, int32_t sq, int32_t hq, int32_t d,
+                             float* delta, void* stream) {
+  if (!o || !dout || !delta) return MMSP_ERR_NULL;
+  if (sq <= 0 || hq <= 0) return MMSP_ERR_SHAPE;
+  if (bad_dim(d)) return MMSP_ERR_UNSUPPORTED;
+  if ((long long)sq * hq * d > kMaxElems) return MMSP_ERR_SHAPE;
+  return check_hip(mmsp::launch_bwd_preprocess(static_cast<const uint16_t*>(o),
+                                               static_cast<const uint16_t*>(dout), sq, hq, d,
+                                               delta, as_stream(stream)));
+}
+
+int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, const float* delta, const int32_t* q_pos,
+                        const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
+                        int32_t d, float scale, uint32_t flags, float* dq_acc, float* dk,
+                        float* dv, void* stream) {
+  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
+  const bool causal = (flags & MMSP_CAUSAL) != 0;
+  if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk || !dv) return MMSP_ERR_NULL;
+  if (causal && (!q_pos || !k_pos)) return MMSP_ERR_NULL;
+  const int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
+  if (st != MMSP_OK) return st;
+  mmsp::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.delta = delta;
+  p.q_pos = q_pos;
+  p.k_pos = k_pos;
+  p.dq = dq_acc;
+  p.dk = dk;
+  p.dv = dv;
+  p.sq = sq;
+  p.sk = sk;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  const int bk = mmsp::bwd_keys_per_block();
+  p.n_ktiles = (sk + bk - 1) / bk;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal ? 1 : 0;
+  p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
+  return check_hip(mmsp::launch_attn_bwd(p, d, as_stream(stream)));
+}
+
+}  // extern "C"

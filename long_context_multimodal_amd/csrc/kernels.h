@@ -1,0 +1,59 @@
+// Host-side launch interface between the C-ABI layer (api.hip) and the
+// kernel translation units.  Parameters arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmsp {
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* q_pos;
+  const int32_t* k_pos;
+  float* o;
+  float* lse;
+  int sq, sk, hq, hkv, group, n_qtiles;
+  float scale_log2;  // scale * log2(e)
+  int causal, accumulate;
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const float* delta;
+  const int32_t* q_pos;
+  const int32_t* k_pos;
+  float* dq;
+  float* dk;
+  float* dv;
+  int sq, sk, hq, hkv, group, n_ktiles;
+  float scale;
+  float scale_log2;
+  int causal, accumulate;
+};
+
+int fwd_rows_per_block();
+hipError_t launch_attn_fwd(const FwdParams& p, int d, hipStream_t stream);
+
+hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part,
+                            const float* lse_part, int sq, int hq, int d, uint16_t* o_bf16,
+                            hipStream_t stream);
+
+hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dout, int sq, int hq, int d,
+                                 float* delta, hipStream_t stream);
+
+int bwd_keys_per_block();
+hipError_t launch_attn_bwd(const BwdParams& p, int d, hipStream_t stream);
+
+// shard balance: vis/owner scratch of n/g int32 each (MODALITY only)
+hipError_t launch_shard_balance(const uint8_t* labels, int n, int n_ranks, int mode, int g,
+                                int32_t* perm, int32_t* inv_perm, int32_t* ws_vis,
+                                int32_t* ws_owner, hipStream_t stream);
+
+}  // namespace mmsp

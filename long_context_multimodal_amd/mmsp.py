@@ -1,0 +1,217 @@
+"""ctypes binding of ``libmmsp.so`` (the C-ABI in ``include/mmsp.h``).
+
+Argument marshalling only: tensors are checked for dtype, device, layout and
+shape, their device pointers and the current HIP stream are handed to the
+library, and a nonzero status raises :class:`MMSPError`.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  torch is
+used for device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmmsp.so")
+
+MMSP_OK = 0
+STATUS_NAMES = {
+    0: "MMSP_OK", -1: "MMSP_ERR_NULL", -2: "MMSP_ERR_SHAPE", -3: "MMSP_ERR_UNSUPPORTED",
+    -4: "MMSP_ERR_DIVISIBILITY", -5: "MMSP_ERR_WORKSPACE", -6: "MMSP_ERR_HIP",
+}
+BALANCE_ZIGZAG, BALANCE_MODALITY = 0, 1
+CAUSAL, ACCUMULATE = 1, 2
+
+# every symbol the header declares, with its ctypes signature
+_VP, _I32, _I64, _U32, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                    ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t)
+SIGNATURES = {
+    "mmsp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mmsp_abi_version": (ctypes.c_int, []),
+    "mmsp_shard_balance_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
+    "mmsp_shard_balance": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "mmsp_attn_fwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
+                                           _F32, _U32, _VP, _VP, _VP]),
+    "mmsp_lse_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "mmsp_attn_bwd_preprocess": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "mmsp_attn_bwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
+                                           _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
+}
+
+_lib = None
+
+
+class MMSPError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        name = STATUS_NAMES.get(code, str(code))
+        msg = lib().mmsp_status_string(code).decode()
+        super().__init__(f"{where}: {name} ({msg})")
+
+
+def lib():
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_multimodal_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(code: int, where: str):
+    if code != MMSP_OK:
+        raise MMSPError(code, where)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, name, ndim=None):
+    import torch
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    del torch
+
+
+# ---------------------------------------------------------------- a1
+def shard_balance(n: int, n_ranks: int, mode: int = BALANCE_ZIGZAG, granularity: int = 0,
+                  labels=None, with_inverse: bool = True, device="cuda"):
+    """Rank-major shard permutation (int32[n]) and optionally its inverse."""
+    import torch
+    if labels is not None:
+        _need(labels, torch.uint8, "labels", 1)
+        if labels.numel() != n:
+            raise ValueError("labels must have n entries")
+    perm = torch.empty(n, dtype=torch.int32, device=device)
+    inv = torch.empty(n, dtype=torch.int32, device=device) if with_inverse else None
+    ws_bytes = lib().mmsp_shard_balance_workspace_bytes(n, n_ranks, mode, granularity)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device) if ws_bytes else None
+    _check(lib().mmsp_shard_balance(_ptr(labels), n, n_ranks, mode, granularity, _ptr(perm),
+                                    _ptr(inv), _ptr(ws), ws_bytes, _stream()),
+           "mmsp_shard_balance")
+    return perm, inv
+
+
+# ---------------------------------------------------------------- a2
+def attn_fwd_chunk(q, k, v, q_pos=None, k_pos=None, scale=None, causal=True, o=None, lse=None,
+                   accumulate=False):
+    """Attention of ``q[sq,hq,d]`` against one chunk ``k, v[sk,hkv,d]`` (bf16).
+
+    Returns ``(o fp32[sq,hq,d], lse fp32[hq,sq])``; with ``accumulate`` the
+    given ``(o, lse)`` are merged with this chunk's result in place.
+    """
+    import torch
+    _need(q, torch.bfloat16, "q", 3)
+    _need(k, torch.bfloat16, "k", 3)
+    _need(v, torch.bfloat16, "v", 3)
+    sq, hq, d = q.shape
+    sk, hkv, dk = k.shape
+    if dk != d or tuple(v.shape) != (sk, hkv, d):
+        raise ValueError("q/k/v shapes disagree")
+    if causal:
+        _need(q_pos, torch.int32, "q_pos", 1)
+        _need(k_pos, torch.int32, "k_pos", 1)
+        if q_pos.numel() != sq or k_pos.numel() != sk:
+            raise ValueError("position arrays must match sq / sk")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if accumulate:
+        if o is None or lse is None:
+            raise ValueError("accumulate needs the running (o, lse)")
+    if o is None:
+        o = torch.empty((sq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, sq), dtype=torch.float32, device=q.device)
+    _need(o, torch.float32, "o", 3)
+    _need(lse, torch.float32, "lse", 2)
+    flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
+    _check(lib().mmsp_attn_fwd_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(q_pos if causal else None),
+                                     _ptr(k_pos if causal else None), sq, sk, hq, hkv, d,
+                                     float(scale), flags, _ptr(o), _ptr(lse), _stream()),
+           "mmsp_attn_fwd_chunk")
+    return o, lse
+
+
+# ---------------------------------------------------------------- a3
+def lse_merge(o_acc, lse_acc, o_part=None, lse_part=None, o_final=None):
+    """Merge ``(o_part, lse_part)`` into ``(o_acc, lse_acc)`` in place.
+
+    ``o_final`` (bf16, optional) receives the merged output rounded to bf16.
+    """
+    import torch
+    _need(o_acc, torch.float32, "o_acc", 3)
+    _need(lse_acc, torch.float32, "lse_acc", 2)
+    _need(o_part, torch.float32, "o_part", 3)
+    _need(lse_part, torch.float32, "lse_part", 2)
+    _need(o_final, torch.bfloat16, "o_final", 3)
+    sq, hq, d = o_acc.shape
+    _check(lib().mmsp_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), sq, hq,
+                                d, _ptr(o_final), _stream()), "mmsp_lse_merge")
+    return o_acc, lse_acc
+
+
+# ---------------------------------------------------------------- a5
+def attn_bwd_preprocess(o, dout, delta=None):
+    """``delta[h, i] = sum_c dout[i,h,c] * o[i,h,c]`` (bf16 in, fp32 out)."""
+    import torch
+    _need(o, torch.bfloat16, "o", 3)
+    _need(dout, torch.bfloat16, "dout", 3)
+    sq, hq, d = o.shape
+    if delta is None:
+        delta = torch.empty((hq, sq), dtype=torch.float32, device=o.device)
+    _check(lib().mmsp_attn_bwd_preprocess(_ptr(o), _ptr(dout), sq, hq, d, _ptr(delta), _stream()),
+           "mmsp_attn_bwd_preprocess")
+    return delta
+
+
+# ---------------------------------------------------------------- a6
+def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=None,
+                   scale=None, causal=True, accumulate=False):
+    """Backward of one chunk: adds to ``dq_acc``; returns ``(dk, dv)`` fp32."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, torch.bfloat16, n, 3)
+    _need(lse, torch.float32, "lse", 2)
+    _need(delta, torch.float32, "delta", 2)
+    _need(dq_acc, torch.float32, "dq_acc", 3)
+    sq, hq, d = q.shape
+    sk, hkv, _ = k.shape
+    if causal:
+        _need(q_pos, torch.int32, "q_pos", 1)
+        _need(k_pos, torch.int32, "k_pos", 1)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dk is None:
+        dk = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
+    flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
+    _check(lib().mmsp_attn_bwd_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                     _ptr(delta), _ptr(q_pos if causal else None),
+                                     _ptr(k_pos if causal else None), sq, sk, hq, hkv, d,
+                                     float(scale), flags, _ptr(dq_acc), _ptr(dk), _ptr(dv),
+                                     _stream()), "mmsp_attn_bwd_chunk")
+    return dk, dv

@@ -1,0 +1,224 @@
+"""GPU parity of the forward chunk kernel, the LSE merge and the ring loop
+against the float64 oracle (same bf16-rounded inputs)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_multimodal_amd.workloads import TINY, bf16_round, normal_bf16
+from tests.helpers import (assert_close_abs, bf16_bits_to_f64, to_dev_bf16, to_dev_i32, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from long_context_multimodal_amd import mmsp, ring
+    mmsp.lib()
+    return mmsp, ring
+
+
+def _tensors(seed, sq, sk, hq, hkv, d, n_chunks=1, qscale=1.0):
+    qb, qv = normal_bf16(seed, (sq, hq, d), scale=qscale)
+    kb, kv = normal_bf16(seed + 100, (n_chunks, sk, hkv, d))
+    vb, vv = normal_bf16(seed + 200, (n_chunks, sk, hkv, d))
+    return qb, qv, kb, kv, vb, vv
+
+
+def _interleaved_positions(rng, sq, sk, lo_q=0):
+    allpos = np.sort(rng.choice(3 * (sq + sk), size=sq + sk, replace=False))
+    sel = np.zeros(sq + sk, bool)
+    sel[rng.choice(sq + sk, size=sq, replace=False)] = True
+    return allpos[sel].astype(np.int32), allpos[~sel].astype(np.int32)
+
+
+def _run_chunk(mm, qb, kb, vb, qp, kp, causal=True, scale=None):
+    mmsp, _ = mm
+    q, k, v = to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb)
+    o, lse = mmsp.attn_fwd_chunk(q, k, v, to_dev_i32(qp) if causal else None,
+                                 to_dev_i32(kp) if causal else None, scale=scale, causal=causal)
+    return to_np(o), to_np(lse)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (7, 1), (8, 1)])
+def test_chunk_ragged_interleaved(mm, d, hq, hkv):
+    sq, sk = 300, 333  # several tiles and a ragged tail on both sides
+    rng = np.random.default_rng(10 + d + hq + hkv)
+    qp, kp = _interleaved_positions(rng, sq, sk)
+    qb, qv, kb, kv, vb, vv = _tensors(d + hq, sq, sk, hq, hkv, d)
+    o, lse = _run_chunk(mm, qb, kb[0], vb[0], qp, kp)
+    o_ref, l_ref = oracle.attention_forward(qv, kv[0], vv[0], qp, kp)
+    assert_close_abs(o, o_ref, what="O")
+    assert_close_abs(lse, l_ref, what="LSE")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_non_causal(mm, d):
+    qb, qv, kb, kv, vb, vv = _tensors(3, 130, 77, 4, 2, d)
+    o, lse = _run_chunk(mm, qb, kb[0], vb[0], None, None, causal=False)
+    big = np.full(130, 10 ** 6)
+    o_ref, l_ref = oracle.attention_forward(qv, kv[0], vv[0], big, np.arange(77))
+    assert_close_abs(o, o_ref, what="O")
+    assert_close_abs(lse, l_ref, what="LSE")
+
+
+def test_chunk_fully_masked_rows_and_tiles(mm):
+    # queries 0..199 at positions below every key: O = 0 exactly, LSE = -inf
+    sq, sk, d = 400, 256, 128
+    qp = np.concatenate([np.arange(200), 1000 + 3 * np.arange(200)]).astype(np.int32)
+    kp = (1000 + 2 * np.arange(sk)).astype(np.int32)
+    qb, qv, kb, kv, vb, vv = _tensors(5, sq, sk, 4, 4, d)
+    o, lse = _run_chunk(mm, qb, kb[0], vb[0], qp, kp)
+    assert np.all(o[:200] == 0) and np.all(np.isneginf(lse[:, :200]))
+    o_ref, l_ref = oracle.attention_forward(qv, kv[0], vv[0], qp, kp)
+    assert_close_abs(o, o_ref, what="O")
+    assert_close_abs(lse, l_ref, what="LSE")
+
+
+def test_chunk_peaked_softmax(mm):
+    # Q x 4 makes the softmax peaked and stresses the running-max rescale
+    sq = sk = 512
+    pos = np.arange(sq, dtype=np.int32)
+    qb, qv, kb, kv, vb, vv = _tensors(7, sq, sk, 4, 4, 128, qscale=4.0)
+    o, lse = _run_chunk(mm, qb, kb[0], vb[0], pos, pos)
+    o_ref, l_ref = oracle.attention_forward(qv, kv[0], vv[0], pos, pos)
+    assert_close_abs(o, o_ref, what="O")
+    assert_close_abs(lse, l_ref, what="LSE")
+
+
+def test_chunk_first_query_returns_its_value_row(mm):
+    # the query at position 0 sees one key: its output is that key's V row
+    sq, sk, d = 64, 64, 128
+    pos = np.arange(sq, dtype=np.int32)
+    qb, qv, kb, kv, vb, vv = _tensors(9, sq, sk, 2, 2, d)
+    o, lse = _run_chunk(mm, qb, kb[0], vb[0], pos, pos)
+    np.testing.assert_allclose(o[0], vv[0][0], rtol=1e-6, atol=0)
+    s0 = (qv[0] * kv[0][0]).sum(-1) / math.sqrt(d)
+    np.testing.assert_allclose(lse[:, 0], s0, rtol=0, atol=1e-5)
+
+
+def test_chunk_explicit_scale(mm):
+    sq, sk, d = 200, 200, 64
+    pos = np.arange(sq, dtype=np.int32)
+    qb, qv, kb, kv, vb, vv = _tensors(11, sq, sk, 2, 2, d)
+    o, lse = _run_chunk(mm, qb, kb[0], vb[0], pos, pos, scale=0.05)
+    o_ref, l_ref = oracle.attention_forward(qv, kv[0], vv[0], pos, pos, scale=0.05)
+    assert_close_abs(o, o_ref, what="O")
+    assert_close_abs(lse, l_ref, what="LSE")
+
+
+def _tiny_inputs():
+    w = TINY
+    qb, qv = w.q()
+    kb, kv = w.k()
+    vb, vv = w.v()
+    pos = np.arange(w.n_tokens, dtype=np.int32)
+    kps = [pos[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
+    return w, qb, qv, kb, kv, vb, vv, pos, kps
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_tiny_ring_forward(mm, fused):
+    mmsp, ring = mm
+    w, qb, qv, kb, kv, vb, vv, pos, kps = _tiny_inputs()
+    ks = [to_dev_bf16(kb[c]) for c in range(w.n_chunks)]
+    vs = [to_dev_bf16(vb[c]) for c in range(w.n_chunks)]
+    o, lse, o16 = ring.ring_forward(to_dev_bf16(qb), ks, vs, to_dev_i32(pos),
+                                    [to_dev_i32(k) for k in kps], rank=0, fused=fused)
+    o_ref, l_ref = oracle.ring_forward(qv, list(kv), list(vv), pos, kps)
+    assert_close_abs(to_np(o), o_ref, what="O_acc")
+    assert_close_abs(to_np(lse), l_ref, what="LSE")
+    # the final bf16 output is the RNE rounding of the fp32 accumulator
+    bits, _ = bf16_round(to_np(o))
+    assert np.array_equal(to_np(o16), bits)
+    # every chunk alone, too
+    for c in range(w.n_chunks):
+        oc, lc = _run_chunk(mm, qb, kb[c], vb[c], pos, kps[c])
+        oc_ref, lc_ref = oracle.attention_forward(qv, kv[c], vv[c], pos, kps[c])
+        assert_close_abs(oc, oc_ref, what=f"O chunk {c}")
+        assert_close_abs(lc, lc_ref, what=f"LSE chunk {c}")
+
+
+def test_merge_kernel_vs_oracle(mm):
+    mmsp, _ = mm
+    import torch
+    rng = np.random.default_rng(21)
+    sq, hq, d = 257, 3, 128
+    oa = rng.standard_normal((sq, hq, d)).astype(np.float32)
+    ob = rng.standard_normal((sq, hq, d)).astype(np.float32)
+    la = (rng.standard_normal((hq, sq)) * 4).astype(np.float32)
+    lb = (rng.standard_normal((hq, sq)) * 4).astype(np.float32)
+    la[0, :10] = -np.inf
+    lb[0, 5:15] = -np.inf
+    oa[:10, 0] = 0
+    ob[5:15, 0] = 0
+    o_acc = torch.from_numpy(oa.copy()).cuda()
+    l_acc = torch.from_numpy(la.copy()).cuda()
+    o16 = torch.empty((sq, hq, d), dtype=torch.bfloat16, device="cuda")
+    mmsp.lse_merge(o_acc, l_acc, torch.from_numpy(ob).cuda(), torch.from_numpy(lb).cuda(),
+                   o_final=o16)
+    o_ref, l_ref = oracle.lse_merge(oa, la, ob, lb)
+    assert_close_abs(to_np(o_acc), o_ref, max_abs=1e-5, mean_abs=1e-6, what="O")
+    assert_close_abs(to_np(l_acc), l_ref, max_abs=1e-5, mean_abs=1e-6, what="LSE")
+    assert np.all(to_np(o_acc)[5:10, 0] == 0)  # both empty: (0, -inf), no NaN
+    bits, _ = bf16_round(to_np(o_acc))
+    assert np.array_equal(to_np(o16), bits)
+
+
+def test_ring_order_independence_and_replay(mm):
+    mmsp, ring = mm
+    w, qb, qv, kb, kv, vb, vv, pos, kps = _tiny_inputs()
+    q = to_dev_bf16(qb)
+    ks = [to_dev_bf16(kb[c]) for c in range(4)]
+    vs = [to_dev_bf16(vb[c]) for c in range(4)]
+    qp, kpd = to_dev_i32(pos), [to_dev_i32(k) for k in kps]
+    o_ref, l_ref = oracle.ring_forward(qv, list(kv), list(vv), pos, kps)
+    for order in ([0, 3, 2, 1], [2, 0, 3, 1], [3, 2, 1, 0]):
+        o, lse, _ = ring.ring_forward(q, ks, vs, qp, kpd, order=order)
+        assert_close_abs(to_np(o), o_ref, what=f"O order {order}")
+        assert_close_abs(to_np(lse), l_ref, what=f"LSE order {order}")
+    # a dropped step replayed last gives the same result
+    o, lse, _ = ring.ring_forward(q, ks, vs, qp, kpd, order=[0, 1, 3, 2])
+    assert_close_abs(to_np(o), o_ref, what="O replay")
+    # a step merged twice is visible in LSE: rows chunk 3 reaches rise by
+    # ln(1 + exp(L3 - L)) (ln 2 where it is the only contributor), others stay
+    o2, l2, _ = ring.ring_forward(q, ks, vs, qp, kpd, order=[0, 1, 2, 3, 3])
+    _, l3 = oracle.attention_forward(qv, kv[3], vv[3], pos, kps[3])
+    want = np.logaddexp(l_ref, l3)
+    assert_close_abs(to_np(l2), want, max_abs=1e-4, mean_abs=1e-5, what="LSE twice")
+    reach = pos >= 768
+    assert np.all(to_np(l2)[:, reach] > to_np(lse)[:, reach])
+
+
+def test_resume_after_k_steps_is_bitwise_identical(mm):
+    mmsp, ring = mm
+    import torch
+    w, qb, qv, kb, kv, vb, vv, pos, kps = _tiny_inputs()
+    q = to_dev_bf16(qb)
+    ks = [to_dev_bf16(kb[c]) for c in range(4)]
+    vs = [to_dev_bf16(vb[c]) for c in range(4)]
+    qp, kpd = to_dev_i32(pos), [to_dev_i32(k) for k in kps]
+    o_full, l_full, _ = ring.ring_forward(q, ks, vs, qp, kpd)
+    o, lse = mmsp.attn_fwd_chunk(q, ks[0], vs[0], qp, kpd[0])
+    mmsp.attn_fwd_chunk(q, ks[3], vs[3], qp, kpd[3], o=o, lse=lse, accumulate=True)
+    state = (to_np(o).copy(), to_np(lse).copy())  # checkpoint after 2 of 4 steps
+    o = torch.from_numpy(state[0]).cuda()
+    lse = torch.from_numpy(state[1]).cuda()
+    for c in (2, 1):
+        mmsp.attn_fwd_chunk(q, ks[c], vs[c], qp, kpd[c], o=o, lse=lse, accumulate=True)
+    assert np.array_equal(to_np(o), to_np(o_full))
+    assert np.array_equal(to_np(lse), to_np(l_full))
+
+
+def test_forward_is_deterministic(mm):
+    sq = sk = 700
+    pos = np.arange(sq, dtype=np.int32)
+    qb, qv, kb, kv, vb, vv = _tensors(13, sq, sk, 4, 2, 128)
+    a = _run_chunk(mm, qb, kb[0], vb[0], pos, pos)
+    b = _run_chunk(mm, qb, kb[0], vb[0], pos, pos)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
