@@ -1,0 +1,341 @@
+"""Throughput of one rank's MM-SP chunked causal attention on one MI355X.
+
+One step is one pass of the whole per-rank hot path over one batch of
+synthetic input: shard balance (positions of every rank), the forward over all
+KV chunks in ring order with the LSE merge fused into each chunk's epilogue,
+the bf16 output, the backward preprocess and the backward over all chunks.
+Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line.  ``value`` is forward+backward TFLOP/s of the step
+(algorithmic FLOPs over visible (q, k) pairs only: 4*d per pair and query head
+forward, 10*d backward); the forward alone is reported beside it.  The
+``roofline`` object covers the dominant kernel (per-launch HIP events on the
+launch stream); ``cpu_baseline`` times the float64 oracle on a bounded sample
+(the first few query heads of the same workload) on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from long_context_multimodal_amd.workloads import WORKLOADS, TRAIN  # noqa: E402
+
+METRIC = "causal attn TFLOP/s per rank shard (fwd, fwd+bwd); % of MI355X bf16 MFMA peak"
+# MI355X dense bf16 MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz (published 2.5 PFLOP/s)
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = {
+    "attn_bwd_chunk": "long_context_multimodal_amd/csrc/attn_bwd.hip",
+    "attn_fwd_chunk": "long_context_multimodal_amd/csrc/attn_fwd.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class LaunchTimer:
+    """HIP events around every chunk launch on the current (launch) stream."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.open = {}
+        self.done = {"fwd": [], "bwd": []}
+        self.enabled = False
+
+    def start(self, kind, chunk):
+        if not self.enabled:
+            return
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.open[(kind, chunk)] = e
+
+    def stop(self, kind, chunk):
+        if not self.enabled:
+            return
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.done[kind].append((chunk, self.open.pop((kind, chunk)), e))
+
+    def summary(self, kind):
+        ms = [(c, a.elapsed_time(b)) for c, a, b in self.done[kind]]
+        return ms
+
+
+def rank_positions(perm, w, rank):
+    shard = w.shard
+    return perm[rank * shard:(rank + 1) * shard]
+
+
+def build_inputs(w, device):
+    """Seeded synthetic tensors of the workload, moved to HBM."""
+    import torch
+    t0 = time.time()
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(device)
+
+    qb, _ = w.q()
+    q = dev(qb)
+    del qb
+    kb, _ = w.k()
+    ks = [dev(kb[c]) for c in range(w.n_chunks)]
+    del kb
+    vb, _ = w.v()
+    vs = [dev(vb[c]) for c in range(w.n_chunks)]
+    del vb
+    dout = None
+    if w.backward:
+        gb, _ = w.do()
+        dout = dev(gb)
+        del gb
+    labels = torch.from_numpy(w.labels()).to(device)
+    log(f"[bench] inputs of {w.name} generated and resident in {time.time() - t0:.1f}s")
+    return q, ks, vs, dout, labels
+
+
+def visible_pairs_per_chunk(w, perm_np, rank):
+    """Visible (q, k) pairs per query head for every chunk (host, from positions)."""
+    qp = np.sort(rank_positions(perm_np, w, rank))
+    out = []
+    for c in range(w.n_chunks):
+        kp = np.sort(perm_np[c * w.chunk:(c + 1) * w.chunk])
+        out.append(int(np.searchsorted(kp, qp, side="right").sum()))
+    return out
+
+
+def source_sha(path):
+    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = source_sha(KERNEL_SRC[kernel])
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith(kernel + " "):
+            continue
+        kv = dict(tok.split("=", 1) for tok in line.split()[1:] if "=" in tok)
+        if kv.get("src_sha") != sha:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    return None
+
+
+def cpu_baseline(w, rank, perm_np):
+    """The oracle, as it stands, on a few query heads of the workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    t_gen = time.time()
+    _, qv = w.q()
+    _, kv = w.k()
+    _, vv = w.v()
+    gv = w.do()[1] if w.backward else None
+    # whole GQA groups (contiguous query heads and the KV heads they read)
+    g = w.hq // w.hkv
+    target = 4 if w.backward else 8
+    nkv = max(1, min(w.hkv, round(target / g)))
+    nh = nkv * g
+    q1 = np.ascontiguousarray(qv[:, :nh, :])
+    k1 = [np.ascontiguousarray(kv[c][:, :nkv, :]) for c in range(w.n_chunks)]
+    v1 = [np.ascontiguousarray(vv[c][:, :nkv, :]) for c in range(w.n_chunks)]
+    g1 = np.ascontiguousarray(gv[:, :nh, :]) if gv is not None else None
+    del qv, kv, vv, gv
+    qp = rank_positions(perm_np, w, rank)
+    kps = [perm_np[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
+    order = [(rank - t) % w.n_chunks for t in range(w.n_chunks)]
+    log(f"[bench] cpu_baseline inputs ready in {time.time() - t_gen:.1f}s")
+    t0 = time.time()
+    o, lse = oracle.ring_forward(q1, k1, v1, qp, kps, order=order)
+    t_fwd = time.time() - t0
+    t_bwd = 0.0
+    if g1 is not None:
+        t1 = time.time()
+        delta = oracle.bwd_delta(o, g1)
+        for c in order:
+            oracle.attention_backward(q1, k1[c], v1[c], g1, lse, delta, qp, kps[c])
+        t_bwd = time.time() - t1
+    pairs = sum(visible_pairs_per_chunk(w, perm_np, rank))
+    flops = (4 + (10 if w.backward else 0)) * w.d * pairs * nh
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    elapsed = t_fwd + t_bwd
+    return {
+        "value": round(flops / elapsed / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"query heads 0-{nh - 1} of {w.hq} ({nh}/{w.hq} of the step's FLOPs), all "
+                   f"{w.shard} query "
+                   f"rows, all {w.n_chunks} chunks, forward{' + backward' if w.backward else ''}; "
+                   f"fwd {t_fwd:.1f}s bwd {t_bwd:.1f}s; host affinity "
+                   f"{len(os.sched_getaffinity(0))} cpus, BLAS threads {threads}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=TRAIN.name, choices=sorted(WORKLOADS))
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--unfused", action="store_true", help="separate merge pass per chunk")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the ring (one rank); --gpus {args.gpus} is "
+              "not supported: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_multimodal_amd import mmsp, ring
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mmsp.lib()
+    device = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    rank = args.rank
+    q, ks, vs, dout, labels = build_inputs(w, device)
+
+    n = w.n_tokens
+    mode = {"zigzag": mmsp.BALANCE_ZIGZAG, "modality": mmsp.BALANCE_MODALITY}.get(w.layout)
+
+    # buffers reused by every step
+    sq, hq, d = q.shape
+    o = torch.empty((sq, hq, d), dtype=torch.float32, device=device)
+    lse = torch.empty((hq, sq), dtype=torch.float32, device=device)
+    o16 = torch.empty((sq, hq, d), dtype=torch.bfloat16, device=device)
+    delta = torch.empty((hq, sq), dtype=torch.float32, device=device)
+    dq = torch.empty((sq, hq, d), dtype=torch.float32, device=device) if w.backward else None
+    dks = [torch.empty(k.shape, dtype=torch.float32, device=device) for k in ks] \
+        if w.backward else None
+    dvs = [torch.empty(k.shape, dtype=torch.float32, device=device) for k in ks] \
+        if w.backward else None
+    contiguous_pos = torch.arange(n, dtype=torch.int32, device=device)
+    timer = LaunchTimer()
+
+    def step():
+        if mode is None:  # single rank holding every position, contiguous chunks
+            perm = contiguous_pos
+        else:
+            perm, _ = mmsp.shard_balance(n, w.n_ranks, mode, w.granularity,
+                                         labels=labels if mode == mmsp.BALANCE_MODALITY else None,
+                                         with_inverse=False)
+        qp = perm[rank * w.shard:(rank + 1) * w.shard]
+        kps = [perm[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
+        ring.ring_forward(q, ks, vs, qp, kps, rank=rank, fused=not args.unfused, o=o, lse=lse,
+                          o_final=o16, timer=timer)
+        if w.backward:
+            ring.ring_backward(q, ks, vs, dout, o16, lse, qp, kps, rank=rank, dq=dq, dks=dks,
+                               dvs=dvs, delta=delta, timer=timer)
+        return perm
+
+    log(f"[bench] warmup {args.warmup} steps")
+    perm = None
+    for _ in range(args.warmup):
+        perm = step()
+    torch.cuda.synchronize()
+    perm_np = perm.cpu().numpy() if perm is not None else step().cpu().numpy()
+
+    # timed region: barrier (one process) + synchronize on both sides
+    timer.enabled = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timer.enabled = False
+    ms_per_step = elapsed / args.steps * 1e3
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    pairs = visible_pairs_per_chunk(w, perm_np, rank)
+    fwd_flops = 4.0 * d * hq * sum(pairs)
+    bwd_flops = 10.0 * d * hq * sum(pairs) if w.backward else 0.0
+    total_flops = fwd_flops + bwd_flops
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    def kernel_roofline(kind, per_pair):
+        launches = timer.summary(kind)
+        if not launches:
+            return None
+        tot_ms = sum(ms for _, ms in launches)
+        tot_flop = sum(per_pair * d * hq * pairs[c] for c, _ in launches)
+        avg_ms = tot_ms / len(launches)
+        achieved = tot_flop / (tot_ms * 1e-3) / 1e12
+        name = "attn_bwd_chunk" if kind == "bwd" else "attn_fwd_chunk"
+        traffic = read_traffic(name)
+        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "avg_launch_ms": round(avg_ms, 4),
+                "launches": len(launches),
+                "algorithmic_flop_per_launch": round(tot_flop / len(launches), 1)}
+
+    fwd_rf = kernel_roofline("fwd", 4)
+    bwd_rf = kernel_roofline("bwd", 10) if w.backward else None
+    fwd_ms = sum(ms for _, ms in timer.summary("fwd")) / args.steps
+    bwd_ms = sum(ms for _, ms in timer.summary("bwd")) / args.steps if w.backward else 0.0
+    fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
+    if not w.backward:
+        value = fwd_flops / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) rounded to bf16; frame/text label stream)",
+        "config": {
+            "workload": w.name,
+            "description": w.note,
+            "q_shard_tokens": w.shard,
+            "kv_chunks": w.n_chunks,
+            "kv_chunk_tokens": w.chunk,
+            "hq": w.hq, "hkv": w.hkv, "head_dim": w.d,
+            "layout": w.layout, "rank": rank,
+            "pass": "fwd+bwd" if w.backward else "fwd",
+            "merge": "separate" if args.unfused else "fused into chunk epilogue",
+        },
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_tflops, 2) if fwd_tflops else None,
+        "fwd_pct_of_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2) if fwd_tflops else None,
+        "fwd_ms_per_step": round(fwd_ms, 4),
+        "bwd_ms_per_step": round(bwd_ms, 4),
+        "algorithmic_tflop_per_step": round(total_flops / 1e12, 4),
+        "visible_pairs_per_head": int(sum(pairs)),
+        "roofline": bwd_rf if bwd_rf is not None else fwd_rf,
+        "roofline_fwd": fwd_rf,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host (bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(w, rank, perm_np)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

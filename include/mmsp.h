@@ -140,9 +140,11 @@ int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const floa
 /* ---- a5: backward preprocess ----------------------------------------------
  * delta[h][i] = sum_c dout[i][h][c] * o[i][h][c] (fp32 accumulation) from the
  * saved final output; o, dout bf16 [sq][hq][d]; delta fp32 [hq][sq].
+ * dq_zero (nullable) fp32 [sq][hq][d] is set to 0 in the same pass, ready to
+ * be the dq_acc of the following mmsp_attn_bwd_chunk calls.
  */
 int mmsp_attn_bwd_preprocess(const void* o, const void* dout, int32_t sq, int32_t hq, int32_t d,
-                             float* delta, void* stream);
+                             float* delta, float* dq_zero, void* stream);
 
 /* ---- a6: backward of one chunk from the saved final LSE --------------------
  * Training without gradient checkpointing ("LongVILA - ... (Jason's Study)",

@@ -125,14 +125,14 @@ int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const floa
 }
 
 int mmsp_attn_bwd_preprocess(const void* o, const void* dout, int32_t sq, int32_t hq, int32_t d,
-                             float* delta, void* stream) {
+                             float* delta, float* dq_zero, void* stream) {
   if (!o || !dout || !delta) return MMSP_ERR_NULL;
   if (sq <= 0 || hq <= 0) return MMSP_ERR_SHAPE;
   if (bad_dim(d)) return MMSP_ERR_UNSUPPORTED;
   if ((long long)sq * hq * d > kMaxElems) return MMSP_ERR_SHAPE;
   return check_hip(mmsp::launch_bwd_preprocess(static_cast<const uint16_t*>(o),
                                                static_cast<const uint16_t*>(dout), sq, hq, d,
-                                               delta, as_stream(stream)));
+                                               delta, dq_zero, as_stream(stream)));
 }
 
 int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void* dout,

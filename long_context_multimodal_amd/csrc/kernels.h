@@ -46,7 +46,7 @@ hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part,
                             hipStream_t stream);
 
 hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dout, int sq, int hq, int d,
-                                 float* delta, hipStream_t stream);
+                                 float* delta, float* dq_zero, hipStream_t stream);
 
 int bwd_keys_per_block();
 hipError_t launch_attn_bwd(const BwdParams& p, int d, hipStream_t stream);

@@ -58,12 +58,14 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(float* __restrict__ o_ac
 }
 
 // delta[h][i] = sum_c dout[i][h][c] * o[i][h][c]; 16 threads per row, 8 bf16
-// of each operand per thread, reduced with cross-lane adds.
+// of each operand per thread, reduced with cross-lane adds.  Optionally
+// zeroes the same 8 elements of the fp32 dQ accumulator.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __restrict__ o,
                                                              const uint16_t* __restrict__ dout,
                                                              int sq, int hq,
-                                                             float* __restrict__ delta) {
+                                                             float* __restrict__ delta,
+                                                             float* __restrict__ dq_zero) {
   constexpr int TPR = D / 8;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long rows = (long long)sq * hq;
@@ -71,6 +73,11 @@ __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __r
   const int c8 = (int)(idx % TPR);
   float acc = 0.f;
   if (r < rows) {
+    if (dq_zero != nullptr) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)(dq_zero + r * D + 8 * c8) = z;
+      *(f32x4*)(dq_zero + r * D + 8 * c8 + 4) = z;
+    }
     const u32x4 a = *(const u32x4*)(o + r * D + 8 * c8);
     const u32x4 b = *(const u32x4*)(dout + r * D + 8 * c8);
 #pragma unroll
@@ -104,15 +111,15 @@ hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part,
 }
 
 hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dout, int sq, int hq, int d,
-                                 float* delta, hipStream_t stream) {
+                                 float* delta, float* dq_zero, hipStream_t stream) {
   const long long threads = (long long)sq * hq * (d / 8);
   const unsigned grid = (unsigned)((threads + 255) / 256);
   if (d == 64)
     hipLaunchKernelGGL(bwd_preprocess_kernel<64>, dim3(grid), dim3(256), 0, stream, o, dout, sq,
-                       hq, delta);
+                       hq, delta, dq_zero);
   else
     hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(grid), dim3(256), 0, stream, o, dout, sq,
-                       hq, delta);
+                       hq, delta, dq_zero);
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ SIGNATURES = {
     "mmsp_attn_fwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                                            _F32, _U32, _VP, _VP, _VP]),
     "mmsp_lse_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP]),
-    "mmsp_attn_bwd_preprocess": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "mmsp_attn_bwd_preprocess": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP]),
     "mmsp_attn_bwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
                                            _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
 }
@@ -174,15 +174,20 @@ def lse_merge(o_acc, lse_acc, o_part=None, lse_part=None, o_final=None):
 
 
 # ---------------------------------------------------------------- a5
-def attn_bwd_preprocess(o, dout, delta=None):
-    """``delta[h, i] = sum_c dout[i,h,c] * o[i,h,c]`` (bf16 in, fp32 out)."""
+def attn_bwd_preprocess(o, dout, delta=None, dq_zero=None):
+    """``delta[h, i] = sum_c dout[i,h,c] * o[i,h,c]`` (bf16 in, fp32 out).
+
+    ``dq_zero`` (fp32 ``[sq,hq,d]``, optional) is zeroed in the same pass.
+    """
     import torch
     _need(o, torch.bfloat16, "o", 3)
     _need(dout, torch.bfloat16, "dout", 3)
+    _need(dq_zero, torch.float32, "dq_zero", 3)
     sq, hq, d = o.shape
     if delta is None:
         delta = torch.empty((hq, sq), dtype=torch.float32, device=o.device)
-    _check(lib().mmsp_attn_bwd_preprocess(_ptr(o), _ptr(dout), sq, hq, d, _ptr(delta), _stream()),
+    _check(lib().mmsp_attn_bwd_preprocess(_ptr(o), _ptr(dout), sq, hq, d, _ptr(delta),
+                                          _ptr(dq_zero), _stream()),
            "mmsp_attn_bwd_preprocess")
     return delta
 

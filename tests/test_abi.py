@@ -91,9 +91,9 @@ def test_merge_and_preprocess_reject():
     assert lib.mmsp_lse_merge(FAKE, FAKE, FAKE, FAKE, 8, 2, 48, None, None) == -3
     # no operand and no bf16 output: nothing to do, nothing launched
     assert lib.mmsp_lse_merge(FAKE, FAKE, None, None, 8, 2, 64, None, None) == 0
-    assert lib.mmsp_attn_bwd_preprocess(FAKE, None, 8, 2, 64, FAKE, None) == -1
-    assert lib.mmsp_attn_bwd_preprocess(FAKE, FAKE, 8, -2, 64, FAKE, None) == -2
-    assert lib.mmsp_attn_bwd_preprocess(FAKE, FAKE, 8, 2, 100, FAKE, None) == -3
+    assert lib.mmsp_attn_bwd_preprocess(FAKE, None, 8, 2, 64, FAKE, None, None) == -1
+    assert lib.mmsp_attn_bwd_preprocess(FAKE, FAKE, 8, -2, 64, FAKE, None, None) == -2
+    assert lib.mmsp_attn_bwd_preprocess(FAKE, FAKE, 8, 2, 100, FAKE, None, None) == -3
 
 
 def test_shard_balance_rejects_and_workspace():

@@ -33,9 +33,12 @@ def test_preprocess_matches_definition(mm, d):
     sq, hq = 333, 5
     ob, ov = normal_bf16(31, (sq, hq, d))
     gb, gv = normal_bf16(32, (sq, hq, d))
-    delta = mmsp.attn_bwd_preprocess(to_dev_bf16(ob), to_dev_bf16(gb))
+    import torch
+    dq = torch.full((sq, hq, d), 7.0, dtype=torch.float32, device="cuda")
+    delta = mmsp.attn_bwd_preprocess(to_dev_bf16(ob), to_dev_bf16(gb), dq_zero=dq)
     want = oracle.bwd_delta(ov, gv)
     np.testing.assert_allclose(to_np(delta), want, rtol=1e-5, atol=1e-5)
+    assert np.all(to_np(dq) == 0)
 
 
 def _interleaved(rng, sq, sk):
