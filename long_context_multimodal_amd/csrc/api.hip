@@ -164,7 +164,9 @@ int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void*
   p.hkv = hkv;
   p.group = hq / hkv;
   const int bk = mmsp::bwd_keys_per_block();
+  const int bq = mmsp::bwd_rows_per_block();
   p.n_ktiles = (sk + bk - 1) / bk;
+  p.n_qtiles = (sq + bq - 1) / bq;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal ? 1 : 0;

@@ -6,76 +6,57 @@
 // visible pairs, dV = P^T dO, dS = P o (dO V^T - delta), dQ += scale dS K,
 // dK = scale dS^T Q, with dK/dV of a KV head summed over its query heads.
 //
-// Design (one workgroup = 128 keys of one KV head, 4 waves of 32 keys):
-//  * K and V of the wave's 32 keys stay in registers (B operands of
-//    S = Q K^T and dP = dO V^T); the dK^T and dV^T accumulators too;
-//  * the workgroup walks the visible query tiles (32 rows) of every query
-//    head of its KV head; each tile's Q and dO are prefetched into registers
-//    one tile ahead and stored to double-buffered LDS both row-major (A of S
-//    and dP) and transposed in kPerm16 order (A of dK^T and dV^T, whose B
-//    operands are the P / dS accumulators reused in place);
-//  * dS (bf16) goes through LDS once so the four waves can form
-//    dQ = dS K over all 128 keys (each wave one 32-wide slice of the head
-//    dim) and add it to dq with fp32 atomics (two 128-byte lines per
-//    instruction);
-//  * causal skipping: the query range of a workgroup starts at the first
-//    query that can see its first key (binary search); a wave skips tiles it
-//    cannot see and masks only straddling tiles.
+// Two kernels, no atomics:
+//  * dK/dV kernel -- one workgroup = 128 keys of one KV head (4 waves of 32
+//    keys).  K and V of the wave's keys stay in registers as the B operands
+//    of S = Q K^T and dP = dO V^T; the dK^T / dV^T accumulators too.  The
+//    workgroup walks the visible query tiles (32 rows) of every query head
+//    of its KV head; Q and dO tiles arrive by direct global->LDS loads into
+//    swizzled double buffers and serve both as row-major A operands (S, dP)
+//    and, through the transposing LDS read, as Q^T / dO^T (dK^T, dV^T),
+//    whose B operands are the P / dS accumulators reused in place.
+//  * dQ kernel -- one workgroup = 128 query rows of one query head (like the
+//    forward): Q and dO stay in registers, K/V tiles stream through LDS,
+//    S^T = K Q^T and dP^T = V dO^T give P^T and dS^T with the query in the
+//    lane (so LSE and delta are per-lane scalars), and dQ^T += K^T dS^T uses
+//    the transposing read of the K tile.  dQ is added to dq_acc once per
+//    workgroup (plain read-modify-write: each element has one owner).
+// Recomputing S and dP in the dQ kernel costs two extra contractions per
+// visible pair; it replaces fp32 atomics, which on this part execute past
+// the L2 and cost more than the recomputation.
+//
+// Causal skipping in both: the key (or query) range of a workgroup is
+// bounded by a binary search on the sorted positions, waves skip tiles they
+// cannot see and mask only the tiles that straddle their positions.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace mmsp {
 namespace {
 
+// ============================== dK / dV ======================================
 template <int D>
-struct BwdCfg {
+struct DkdvCfg {
   static constexpr int BK = 128;          // keys per workgroup
   static constexpr int BQ = 32;           // queries per tile
   static constexpr int THREADS = 256;
-  static constexpr int KS = D / 16;       // K-steps over the head dim
-  static constexpr int MB = D / 32;       // 32-row blocks of the head dim
-  static constexpr int CPR = D / 8;       // 16-byte chunks per row
-  static constexpr int RSTR = D + 8;      // [q][d] stride (bf16)
-  static constexpr int TSTR = BQ + 8;     // [d][q] stride (bf16)
-  static constexpr int KTSTR = BK + 8;    // K^T [d][key] stride (bf16)
-  static constexpr int SSTR = BK + 8;     // dS [q][key] stride (bf16)
-  static constexpr int QITEMS = (BQ / 4) * CPR;  // (4 rows x 8 dims) items per tensor
+  static constexpr int KS = D / 16;
+  static constexpr int MB = D / 32;
+  static constexpr int TILE = BQ * D * 2;  // bytes of one Q or dO tile
+  static constexpr int VTILE = BK * D * 2; // bytes of the workgroup's V rows
 };
 
-constexpr int kPosInf = 0x7fffffff;
-
-// 4 rows x 8 bf16 (one u32x4 per row) -> 8 rows of 4 bf16, written at
-// base[e * stride] for e = 0..7 (the transposed layout's 8 head-dim rows).
-__device__ __forceinline__ void store_transposed_4x8(uint16_t* base, int stride, const u32x4* r) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1;
-    const uint32_t a0 = r[0][w], a1 = r[1][w], a2 = r[2][w], a3 = r[3][w];
-    u32x2 out;
-    if ((e & 1) == 0) {
-      out[0] = (a0 & 0xffffu) | (a1 << 16);
-      out[1] = (a2 & 0xffffu) | (a3 << 16);
-    } else {
-      out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-      out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-    }
-    *(u32x2*)(base + e * stride) = out;
-  }
-}
-
 template <int D>
-__global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
-  using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * C::KTSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][C::BQ * C::RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][C::BQ * C::RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[2][D * C::TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[2][D * C::TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sdS[2][C::BQ * C::SSTR];
-  __shared__ __attribute__((aligned(16))) float sL[2][C::BQ];   // LSE * log2e (+inf if empty)
-  __shared__ __attribute__((aligned(16))) float sDl[2][C::BQ];  // delta
-  __shared__ __attribute__((aligned(16))) int sQp[2][C::BQ];    // positions (INT_MIN past sq)
+__global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
+  using C = DkdvCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[4 * C::TILE + C::VTILE];  // Q0|Q1|dO0|dO1|V
+  __shared__ __attribute__((aligned(16))) float sL[2][C::BQ];      // LSE*log2e (+inf empty)
+  __shared__ __attribute__((aligned(16))) float sDl[2][C::BQ];     // delta
+  __shared__ __attribute__((aligned(16))) int sQp[2][C::BQ];       // positions
   __shared__ int sQlast[2];
+  lds_char* lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -87,22 +68,21 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
   const int kvh = logical / p.n_ktiles;
   const int kt = logical % p.n_ktiles;  // early keys (more visible queries) first
   const int j0 = kt * C::BK;
-  const int key = j0 + wave * 32 + l32;  // this lane's key
+  const int key = j0 + wave * 32 + l32;
   const bool key_ok = key < p.sk;
   const size_t kv_stride = (size_t)p.hkv * D;
 
-  // ---- key positions of the lane / wave / workgroup ----
   const int kpos = key_ok ? (p.causal ? p.k_pos[key] : 0) : kPosInf;
   const int wk0 = j0 + wave * 32;
   const bool wave_live = wk0 < p.sk;
-  const int wk_last = min(wk0 + 31, p.sk - 1);
   const bool wave_full_keys = wk0 + 31 < p.sk;
   int wkmin = kPosInf, wkmax = kPosInf;
   if (wave_live) {
     wkmin = p.causal ? p.k_pos[wk0] : 0;
-    wkmax = p.causal ? p.k_pos[wk_last] : 0;
+    wkmax = p.causal ? p.k_pos[min(wk0 + 31, p.sk - 1)] : 0;
   }
-  // first query that can see the workgroup's first key
+  wkmin = uniform(wkmin);
+  wkmax = uniform(wkmax);
   int qstart = 0;
   if (p.causal) {
     const int kmin = p.k_pos[j0];
@@ -116,65 +96,57 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
   const int n_qt = (p.sq + C::BQ - 1) / C::BQ;
   const int qt0 = qstart / C::BQ;
   const int per_head = n_qt - qt0;
-  const int total = per_head > 0 ? per_head * p.group : 0;
+  const int total = uniform(per_head > 0 ? per_head * p.group : 0);
 
-  // ---- stationary K, V fragments (B operands, col = key, k = head dim) ----
-  bf16x8 kf[C::KS], vf[C::KS];
+  // stationary K fragments (B operand of S: col = key, k = head dim); the
+  // workgroup's V rows go to LDS once (B operand of dP, read like Q rows)
+  bf16x8 kf[C::KS];
   {
     const uint16_t* kr = p.k + (size_t)key * kv_stride + (size_t)kvh * D + 8 * hh;
-    const uint16_t* vr = p.v + (size_t)key * kv_stride + (size_t)kvh * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (key_ok) {
-        a = *(const u32x4*)(kr + 16 * ks);
-        b = *(const u32x4*)(vr + 16 * ks);
-      }
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (key_ok) a = *(const u32x4*)(kr + 16 * ks);
       kf[ks] = __builtin_bit_cast(bf16x8, a);
-      vf[ks] = __builtin_bit_cast(bf16x8, b);
     }
+    TileLoader<D, C::BK, C::THREADS> vld;
+    vld.init(tid, kv_stride);
+    const uint16_t* vb = p.v + (size_t)j0 * kv_stride + (size_t)kvh * D;
+    if (j0 + C::BK <= p.sk) vld.load(lds + 4 * C::TILE, vb);
+    else vld.load_clamped(lds + 4 * C::TILE, vb, kv_stride, p.sk - j0);
   }
-  // K^T of the workgroup's keys in LDS (natural key order) for dQ = dS K
-  for (int it = tid; it < (C::BK / 4) * C::CPR; it += C::THREADS) {
-    const int kg = it / C::CPR, dc = it % C::CPR;
-    u32x4 r[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = j0 + 4 * kg + e;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (j < p.sk) w = *(const u32x4*)(p.k + (size_t)j * kv_stride + (size_t)kvh * D + dc * 8);
-      r[e] = w;
-    }
-    store_transposed_4x8(&sKt[(8 * dc) * C::KTSTR + 4 * kg], C::KTSTR, r);
-  }
+  const lds_char* vrows = lds + 4 * C::TILE + uniform(wave * 32 * D * 2);
 
-  // ---- query-tile staging ----
-  // threads [0, QITEMS) carry Q, [128, 128 + QITEMS) carry dO: 4 rows x 16 B
-  u32x4 treg[4];
-  float lreg = 0.f, dreg = 0.f;
+  int qoff[C::KS];  // A = Q / dO rows: row l32, chunk 2 ks + hh
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) qoff[ks] = tile_off<D>(l32, 2 * ks + hh);
+  int troff[2][C::MB];  // A = Q^T / dO^T: rows 16 ks + ..., cols 32 mb + l32
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) troff[rh][mb] = tr_offset<D>(lane, 0, rh, mb);
+
+  const size_t q_row_stride = (size_t)p.hq * D;
+  TileLoader<D, C::BQ, C::THREADS> ld;
+  ld.init(tid, q_row_stride);
+  float lreg = INFINITY, dreg = 0.f;
   int preg = INT_MIN;
-  const bool is_q = tid < 128;
-  const int item = is_q ? tid : tid - 128;
-  const bool item_ok = item < C::QITEMS;
-  const int rg = item / C::CPR, dc = item % C::CPR;
 
   auto tile_of = [&](int it, int& h, int& q0) {
     const int gi = it / per_head;
     h = kvh * p.group + gi;
     q0 = (qt0 + it % per_head) * C::BQ;
   };
-  auto load_tile = [&](int it) {
+  auto issue_tile = [&](int it, int buf) {
     int h, q0;
     tile_of(it, h, q0);
-    if (item_ok) {
-      const uint16_t* src = is_q ? p.q : p.dout;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = q0 + 4 * rg + e;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (i < p.sq) w = *(const u32x4*)(src + ((size_t)i * p.hq + h) * D + dc * 8);
-        treg[e] = w;
-      }
+    const size_t o = (size_t)q0 * q_row_stride + (size_t)h * D;
+    if (q0 + C::BQ <= p.sq) {
+      ld.load(lds + buf * C::TILE, p.q + o);
+      ld.load(lds + (2 + buf) * C::TILE, p.dout + o);
+    } else {
+      ld.load_clamped(lds + buf * C::TILE, p.q + o, q_row_stride, p.sq - q0);
+      ld.load_clamped(lds + (2 + buf) * C::TILE, p.dout + o, q_row_stride, p.sq - q0);
     }
     if (tid < C::BQ) {
       const int i = q0 + tid;
@@ -188,28 +160,18 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
         dreg = 0.f;
         preg = INT_MIN;
       }
-    }
-    if (tid == C::BQ) {
-      const int last = min(q0 + C::BQ - 1, p.sq - 1);
-      preg = p.causal ? p.q_pos[last] : (kPosInf - 1);
+    } else if (tid == C::BQ) {
+      preg = p.causal ? p.q_pos[min(q0 + C::BQ - 1, p.sq - 1)] : (kPosInf - 1);
     }
   };
-  auto store_tile = [&](int buf) {
-    if (item_ok) {
-      uint16_t* rm = is_q ? sQ[buf] : sdO[buf];
-      uint16_t* tr = is_q ? sQt[buf] : sdOt[buf];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) *(u32x4*)&rm[(4 * rg + e) * C::RSTR + dc * 8] = treg[e];
-      const int q = 4 * rg;
-      const int col = (q & ~15) + kPerm16(q & 15);
-      store_transposed_4x8(&tr[(8 * dc) * C::TSTR + col], C::TSTR, treg);
-    }
+  auto publish_tile = [&](int buf) {
     if (tid < C::BQ) {
       sL[buf][tid] = lreg;
       sDl[buf][tid] = dreg;
       sQp[buf][tid] = preg;
+    } else if (tid == C::BQ) {
+      sQlast[buf] = preg;
     }
-    if (tid == C::BQ) sQlast[buf] = preg;
   };
 
   f32x16 dkacc[C::MB], dvacc[C::MB];
@@ -220,48 +182,42 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
   }
   const float c = p.scale_log2;
 
-  if (total > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < total; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < total) load_tile(it + 1);
-    int h, q0;
-    tile_of(it, h, q0);
-    const int qfirst = sQp[buf][0];
-    const int qlast = sQlast[buf];
-    uint16_t* ds_out = &sdS[buf][0];
-    const bool vis = wave_live && qlast >= wkmin;
-    if (vis) {
-      const bool full = wave_full_keys && qfirst >= wkmax && (q0 + C::BQ <= p.sq);
+  auto step = [&](auto buf_tag, int it) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (it + 1 < total) issue_tile(it + 1, BUF ^ 1);
+    const lds_char* qt = lds + BUF * C::TILE;
+    const lds_char* dt = lds + (2 + BUF) * C::TILE;
+    const int qfirst = uniform(sQp[BUF][0]);
+    const int qlast = uniform(sQlast[BUF]);
+    if (wave_live && qlast >= wkmin) {
       // S = Q K^T and dP = dO V^T  (row = query, col = key)
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const uint16_t* qr = &sQ[buf][l32 * C::RSTR + 8 * hh];
-      const uint16_t* dr = &sdO[buf][l32 * C::RSTR + 8 * hh];
+      f32x16 s = mfma32x32x16(lds_read_b128(qt, qoff[0]), kf[0], f32x16{});
+      f32x16 dp = mfma32x32x16(lds_read_b128(dt, qoff[0]), lds_read_b128(vrows, qoff[0]),
+                               f32x16{});
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(qr + 16 * ks));
-        s = mfma32x32x16(a, kf[ks], s);
+      for (int ks = 1; ks < C::KS; ++ks) {
+        s = mfma32x32x16(lds_read_b128(qt, qoff[ks]), kf[ks], s);
+        dp = mfma32x32x16(lds_read_b128(dt, qoff[ks]), lds_read_b128(vrows, qoff[ks]), dp);
       }
+      const int last_row_pos = uniform(sQp[BUF][C::BQ - 1]);  // INT_MIN past sq
+      if (!(wave_full_keys && qfirst >= wkmax && last_row_pos != INT_MIN)) {
+        asm volatile("" ::: "memory");
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(dr + 16 * ks));
-        dp = mfma32x32x16(a, vf[ks], dp);
+        for (int i = 0; i < 16; ++i) {
+          const int q = 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (kpos > sQp[BUF][q]) s[i] = -INFINITY;
+        }
       }
       uint32_t pk[8], dsk[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int q = 8 * g + 4 * hh;  // rows q .. q+3 of this lane
-        const f32x4 lq = *(const f32x4*)&sL[buf][q];
-        const f32x4 dq = *(const f32x4*)&sDl[buf][q];
+        const f32x4 lq = *(const f32x4*)&sL[BUF][q];
+        const f32x4 dq = *(const f32x4*)&sDl[BUF][q];
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pe = fast_exp2(fmaf(s[4 * g + e], c, -lq[e]));
-          if (!full && kpos > sQp[buf][q + e]) pe = 0.f;
+          const float pe = fast_exp2(fmaf(s[4 * g + e], c, -lq[e]));
           pv[e] = pe;
           dsv[e] = pe * (dp[4 * g + e] - dq[e]);
         }
@@ -277,57 +233,35 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
         const u32x4 sw = {dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]};
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
         const bf16x8 sb = __builtin_bit_cast(bf16x8, sw);
-        const uint16_t* dot = &sdOt[buf][l32 * C::TSTR + 16 * ks + 8 * hh];
-        const uint16_t* qt = &sQt[buf][l32 * C::TSTR + 16 * ks + 8 * hh];
+        const int rb = ks * 16 * D * 2;
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) {
-          const bf16x8 a1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(dot + mb * 32 * C::TSTR));
-          dvacc[mb] = mfma32x32x16(a1, pb, dvacc[mb]);
-          const bf16x8 a2 = __builtin_bit_cast(bf16x8, *(const u32x4*)(qt + mb * 32 * C::TSTR));
-          dkacc[mb] = mfma32x32x16(a2, sb, dkacc[mb]);
+          dvacc[mb] = mfma32x32x16(lds_read_tr(dt, rb + troff[0][mb], rb + troff[1][mb]), pb,
+                                   dvacc[mb]);
+          dkacc[mb] = mfma32x32x16(lds_read_tr(qt, rb + troff[0][mb], rb + troff[1][mb]), sb,
+                                   dkacc[mb]);
         }
       }
-      // dS -> LDS as [query][key] (natural orders) for dQ = dS K
-      const int kcol = wave * 32 + l32;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = dsk[2 * g + (e >> 1)];
-          ds_out[(8 * g + 4 * hh + e) * C::SSTR + kcol] = (e & 1) ? (uint16_t)(w >> 16)
-                                                                  : (uint16_t)(w & 0xffffu);
-        }
-    } else {
-      const int kcol = wave * 32 + l32;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ds_out[(8 * g + 4 * hh + e) * C::SSTR + kcol] = 0;
     }
-    if (it + 1 < total) store_tile(buf ^ 1);
+    if (it + 1 < total) {
+      publish_tile(BUF ^ 1);
+      wait_vmem();
+    }
     __syncthreads();
-    // dQ[q0 .. q0+32)[32*wave .. +32) += scale * dS K   (row = query, col = head dim);
-    // every tile walked holds a query that sees the workgroup's first key
-    if (wave < C::MB) {
-      f32x16 acc = f32x16{};
-      const uint16_t* ar = &sdS[buf][l32 * C::SSTR + 8 * hh];
-      const uint16_t* br = &sKt[(wave * 32 + l32) * C::KTSTR + 8 * hh];
-#pragma unroll
-      for (int ks = 0; ks < C::BK / 16; ++ks) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(ar + 16 * ks));
-        const bf16x8 b = __builtin_bit_cast(bf16x8, *(const u32x4*)(br + 16 * ks));
-        acc = mfma32x32x16(a, b, acc);
-      }
-      float* dqb = p.dq + (size_t)h * D + wave * 32 + l32;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (q < p.sq) atomicAdd(dqb + (size_t)q * p.hq * D, acc[i] * p.scale);
-      }
-    }
+  };
+
+  if (total > 0) {
+    issue_tile(0, 0);
+    publish_tile(0);
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int it = 0; it < total; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < total) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  // ---- epilogue: dK = scale * dK^T^T, dV = dV^T^T ----
+  // ---- epilogue: dK = scale * (dK^T)^T, dV = (dV^T)^T ----
   if (!key_ok) return;
   float* dkr = p.dk + (size_t)key * kv_stride + (size_t)kvh * D;
   float* dvr = p.dv + (size_t)key * kv_stride + (size_t)kvh * D;
@@ -349,17 +283,222 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
     }
 }
 
+// ================================== dQ =======================================
+template <int D>
+struct DqCfg {
+  static constexpr int BM = 128;
+  static constexpr int BN = 64;
+  static constexpr int THREADS = 256;
+  static constexpr int KS = D / 16;
+  static constexpr int MB = D / 32;
+  static constexpr int NKB = BN / 32;
+  static constexpr int TILE = BN * D * 2;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[4 * C::TILE];  // [K0|K1|V0|V1]
+  __shared__ int sKp[2][C::BN];
+  lds_char* lds = (lds_char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int h = logical / p.n_qtiles;
+  const int qt = p.n_qtiles - 1 - (logical % p.n_qtiles);
+  const int kvh = h / p.group;
+  const int q0 = qt * C::BM;
+  const int row = q0 + wave * 32 + l32;
+  const bool row_ok = row < p.sq;
+
+  int qpos = INT_MIN;
+  float lse2 = INFINITY, delta = 0.f;
+  if (row_ok) {
+    qpos = p.causal ? p.q_pos[row] : (kPosInf - 1);
+    const float l = p.lse[(size_t)h * p.sq + row];
+    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    delta = p.delta[(size_t)h * p.sq + row];
+  }
+  const int wr0 = q0 + wave * 32;
+  const bool wave_live = wr0 < p.sq;
+  int wqmin = 0, wqmax = INT_MIN;
+  if (wave_live) {
+    const int wlast = min(wr0 + 31, p.sq - 1);
+    wqmin = p.causal ? p.q_pos[wr0] : (kPosInf - 1);
+    wqmax = p.causal ? p.q_pos[wlast] : (kPosInf - 1);
+  }
+  wqmin = uniform(wqmin);
+  wqmax = uniform(wqmax);
+  int nk = p.sk;
+  if (p.causal) {
+    const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
+    int lo = 0, hi = p.sk;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.k_pos[mid] <= qmax) lo = mid + 1; else hi = mid;
+    }
+    nk = lo;
+  }
+  const int nt = uniform((nk + C::BN - 1) / C::BN);
+
+  // Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T
+  bf16x8 qf[C::KS], df[C::KS];
+  {
+    const size_t ro = ((size_t)row * p.hq + h) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (row_ok) {
+        a = *(const u32x4*)(p.q + ro + 16 * ks);
+        b = *(const u32x4*)(p.dout + ro + 16 * ks);
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8, a);
+      df[ks] = __builtin_bit_cast(bf16x8, b);
+    }
+  }
+
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = tile_off<D>(l32, 2 * ks + hh);
+  int troff[2][C::MB];
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) troff[rh][mb] = tr_offset<D>(lane, 0, rh, mb);
+
+  const size_t kv_row_stride = (size_t)p.hkv * D;
+  const uint16_t* kbase = p.k + (size_t)kvh * D;
+  const uint16_t* vbase = p.v + (size_t)kvh * D;
+  TileLoader<D, C::BN, C::THREADS> ld;
+  ld.init(tid, kv_row_stride);
+  int kpreg = kPosInf;
+  auto issue_tile = [&](int t, int buf) {
+    const int j0 = t * C::BN;
+    const size_t o = (size_t)j0 * kv_row_stride;
+    if (j0 + C::BN <= p.sk) {
+      ld.load(lds + buf * C::TILE, kbase + o);
+      ld.load(lds + (2 + buf) * C::TILE, vbase + o);
+    } else {
+      ld.load_clamped(lds + buf * C::TILE, kbase + o, kv_row_stride, p.sk - j0);
+      ld.load_clamped(lds + (2 + buf) * C::TILE, vbase + o, kv_row_stride, p.sk - j0);
+    }
+    if (tid < C::BN) {
+      const int j = j0 + tid;
+      kpreg = (j < p.sk) ? (p.causal ? p.k_pos[j] : 0) : kPosInf;
+    }
+  };
+
+  f32x16 dqacc[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) dqacc[mb] = f32x16{};
+  const float c = p.scale_log2;
+
+  auto step = [&](auto buf_tag, int t) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (t + 1 < nt) issue_tile(t + 1, BUF ^ 1);
+    const lds_char* kt = lds + BUF * C::TILE;
+    const lds_char* vt = lds + (2 + BUF) * C::TILE;
+    const int kfirst = uniform(sKp[BUF][0]);
+    const int klast = uniform(sKp[BUF][C::BN - 1]);
+    if (wave_live && kfirst <= wqmax) {
+      const bool straddle = klast > wqmin;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {  // 32 keys at a time
+        const int rb = kb * 32 * D * 2;
+        f32x16 s = mfma32x32x16(lds_read_b128(kt, rb + koff[0]), qf[0], f32x16{});
+        f32x16 dp = mfma32x32x16(lds_read_b128(vt, rb + koff[0]), df[0], f32x16{});
+#pragma unroll
+        for (int ks = 1; ks < C::KS; ++ks) {
+          s = mfma32x32x16(lds_read_b128(kt, rb + koff[ks]), qf[ks], s);
+          dp = mfma32x32x16(lds_read_b128(vt, rb + koff[ks]), df[ks], dp);
+        }
+        if (straddle) {
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (sKp[BUF][key] > qpos) s[i] = -INFINITY;
+          }
+        }
+        uint32_t dsk[8];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = fast_exp2(fmaf(s[i], c, -lse2));
+          const float p1 = fast_exp2(fmaf(s[i + 1], c, -lse2));
+          dsk[i >> 1] = pack_bf16x2(p0 * (dp[i] - delta), p1 * (dp[i + 1] - delta));
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const u32x4 bw = {dsk[4 * half], dsk[4 * half + 1], dsk[4 * half + 2],
+                            dsk[4 * half + 3]};
+          const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+          const int rk = (2 * kb + half) * 16 * D * 2;
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb)
+            dqacc[mb] = mfma32x32x16(lds_read_tr(kt, rk + troff[0][mb], rk + troff[1][mb]), b,
+                                     dqacc[mb]);
+        }
+      }
+    }
+    if (t + 1 < nt) {
+      if (tid < C::BN) sKp[BUF ^ 1][tid] = kpreg;
+      wait_vmem();
+    }
+    __syncthreads();
+  };
+
+  if (nt > 0) {
+    issue_tile(0, 0);
+    if (tid < C::BN) sKp[0][tid] = kpreg;
+    wait_vmem();
+  }
+  __syncthreads();
+  for (int t = 0; t < nt; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nt) step(std::integral_constant<int, 1>{}, t + 1);
+  }
+
+  // ---- epilogue: dq_acc += scale * (dQ^T)^T (this lane owns its elements) ----
+  if (!row_ok || nt == 0) return;
+  float* dqr = p.dq + ((size_t)row * p.hq + h) * D;
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = mb * 32 + 8 * g + 4 * hh;
+      f32x4 v = *(const f32x4*)(dqr + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(p.scale, dqacc[mb][4 * g + e], v[e]);
+      *(f32x4*)(dqr + d0) = v;
+    }
+}
+
+template __global__ void attn_bwd_dkdv_kernel<64>(BwdParams);
+template __global__ void attn_bwd_dkdv_kernel<128>(BwdParams);
+template __global__ void attn_bwd_dq_kernel<64>(BwdParams);
+template __global__ void attn_bwd_dq_kernel<128>(BwdParams);
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(p.n_ktiles * p.hkv), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(p.n_qtiles * p.hq), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-int bwd_keys_per_block() { return BwdCfg<128>::BK; }
+int bwd_keys_per_block() { return DkdvCfg<128>::BK; }
+int bwd_rows_per_block() { return DqCfg<128>::BM; }
 
 hipError_t launch_attn_bwd(const BwdParams& p, int d, hipStream_t stream) {
-  const int grid = p.n_ktiles * p.hkv;
-  if (d == 64)
-    hipLaunchKernelGGL(attn_bwd_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_bwd_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return d == 64 ? launch_bwd_d<64>(p, stream) : launch_bwd_d<128>(p, stream);
 }
 
 }  // namespace mmsp

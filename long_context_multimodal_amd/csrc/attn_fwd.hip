@@ -10,21 +10,24 @@
 //
 // Design (one workgroup = 128 query rows of one query head, 4 waves):
 //  * each wave owns 32 query rows; Q stays in registers for the whole loop;
-//  * K/V tiles of 64 keys are loaded with 16-byte coalesced global loads,
-//    prefetched into registers one tile ahead and stored to a double-buffered
-//    LDS area (K row-major, V transposed with the key order of kPerm16);
+//  * K/V tiles of 64 keys go straight from HBM to a double-buffered,
+//    XOR-swizzled LDS area with 16-byte direct loads (no staging registers);
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a lane holds 16 scores of ONE
 //    query, so the row max/sum are in-lane plus one permlane32 swap;
-//  * O^T += V^T P^T reuses the score registers (converted to bf16) as the B
-//    operand without any data movement;
+//  * O^T += V^T P^T: the score registers, converted to bf16, are the B
+//    operand in place; V^T comes from the row-major V tile through the
+//    transposing LDS read (ds_read_b64_tr_b16);
 //  * online softmax in the log2 domain; the running max is only raised when
 //    a tile's max exceeds it by more than 8 (2^8 headroom in fp32/bf16), so
 //    the O rescale is skipped on most tiles without changing the result;
+//    row sums stay in fp32 (exact LSE for the merge and the backward);
 //  * causal tile skipping from the sorted positions: a binary search bounds
 //    the key range of the workgroup, each wave skips tiles it cannot see and
 //    masks only the tiles that straddle its rows' positions;
 //  * GQA: query head h reads KV head h / G; the workgroup order keeps the
 //    query heads of one KV head on one XCD (shared L2).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -36,24 +39,18 @@ struct FwdCfg {
   static constexpr int BM = 128;
   static constexpr int BN = 64;
   static constexpr int THREADS = 256;
-  static constexpr int KSTR = D + 8;       // bf16 per K row in LDS (16-byte pad)
-  static constexpr int VSTR = BN + 8;      // bf16 per V^T row in LDS
   static constexpr int KS = D / 16;        // K-steps of S^T = K Q^T
   static constexpr int MB = D / 32;        // 32-row blocks of O^T
-  static constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
-  static constexpr int K_LOADS = BN * CPR / THREADS;
-  static constexpr int V_ITEMS = (BN / 4) * CPR;  // (4 keys x 8 dims) items
   static constexpr int NKB = BN / 32;      // 32-key blocks per tile
+  static constexpr int TILE = BN * D * 2;  // bytes of one K or V tile
 };
-
-constexpr int kPosInf = 0x7fffffff;
 
 template <int D, bool ACC>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][C::BN * C::KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * C::VSTR];
+  __shared__ __attribute__((aligned(16))) char smem[4 * C::TILE];
   __shared__ int sKp[2][C::BN];
+  lds_char* lds = (lds_char*)smem;  // [K0 | K1 | V0 | V1]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -80,6 +77,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     wqmin = p.causal ? p.q_pos[wr0] : (kPosInf - 1);
     wqmax = p.causal ? p.q_pos[wlast] : (kPosInf - 1);
   }
+  wqmin = uniform(wqmin);
+  wqmax = uniform(wqmax);
   int nk = p.sk;
   if (p.causal) {
     const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
@@ -90,7 +89,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     }
     nk = lo;
   }
-  const int nt = (nk + C::BN - 1) / C::BN;
+  const int nt = uniform((nk + C::BN - 1) / C::BN);
 
   // ---- Q fragment: B operand of S^T = K Q^T (col = query, k = head dim) ----
   bf16x8 qf[C::KS];
@@ -104,68 +103,37 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- tile staging: global -> registers (prefetch) -> LDS ----
-  u32x4 kreg[C::K_LOADS];
-  u32x4 vreg[4];
-  int kpreg = kPosInf;
+  // ---- per-lane LDS offsets (loop invariant) ----
+  int koff[C::KS];  // K rows l32 (+32 kb), chunk 2 ks + hh
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = tile_off<D>(l32, 2 * ks + hh);
+  int voff[2][C::MB];  // transposing reads of V: rows 16 ks2 + ..., cols 32 mb + l32
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) voff[rh][mb] = tr_offset<D>(lane, 0, rh, mb);
+
+  // ---- tile loads (direct to LDS) ----
   const size_t kv_row_stride = (size_t)p.hkv * D;
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
-
-  auto load_tile = [&](int t) {
+  TileLoader<D, C::BN, C::THREADS> ld;
+  ld.init(tid, kv_row_stride);
+  int kpreg = kPosInf;
+  auto issue_tile = [&](int t, int buf) {
     const int j0 = t * C::BN;
-#pragma unroll
-    for (int c = 0; c < C::K_LOADS; ++c) {
-      const int idx = tid + c * C::THREADS;
-      const int r = idx / C::CPR, cc = idx % C::CPR;
-      const int j = j0 + r;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (j < p.sk) w = *(const u32x4*)(kbase + (size_t)j * kv_row_stride + cc * 8);
-      kreg[c] = w;
-    }
-    if (tid < C::V_ITEMS) {
-      const int kg = tid / C::CPR, dc = tid % C::CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * kg + r;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (j < p.sk) w = *(const u32x4*)(vbase + (size_t)j * kv_row_stride + dc * 8);
-        vreg[r] = w;
-      }
+    const size_t o = (size_t)j0 * kv_row_stride;
+    if (j0 + C::BN <= p.sk) {
+      ld.load(lds + buf * C::TILE, kbase + o);
+      ld.load(lds + (2 + buf) * C::TILE, vbase + o);
+    } else {
+      ld.load_clamped(lds + buf * C::TILE, kbase + o, kv_row_stride, p.sk - j0);
+      ld.load_clamped(lds + (2 + buf) * C::TILE, vbase + o, kv_row_stride, p.sk - j0);
     }
     if (tid < C::BN) {
       const int j = j0 + tid;
       kpreg = (j < p.sk) ? (p.causal ? p.k_pos[j] : 0) : kPosInf;
     }
-  };
-
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < C::K_LOADS; ++c) {
-      const int idx = tid + c * C::THREADS;
-      const int r = idx / C::CPR, cc = idx % C::CPR;
-      *(u32x4*)&sK[buf][r * C::KSTR + cc * 8] = kreg[c];
-    }
-    if (tid < C::V_ITEMS) {
-      const int kg = tid / C::CPR, dc = tid % C::CPR;
-      const int key = 4 * kg;
-      const int col = (key & ~15) + kPerm16(key & 15);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint32_t a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
-        u32x2 out;
-        if ((e & 1) == 0) {
-          out[0] = (a0 & 0xffffu) | (a1 << 16);
-          out[1] = (a2 & 0xffffu) | (a3 << 16);
-        } else {
-          out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-          out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        }
-        *(u32x2*)&sV[buf][(8 * dc + e) * C::VSTR + col] = out;
-      }
-    }
-    if (tid < C::BN) sKp[buf][tid] = kpreg;
   };
 
   f32x16 oacc[C::MB];
@@ -175,37 +143,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   float l_run = 0.f;        // this lane's partial row sum
   const float c = p.scale_log2;
 
-  if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) load_tile(t + 1);
-    const int kfirst = sKp[buf][0];
-    const int klast = sKp[buf][C::BN - 1];
+  // one K/V tile; BUF is a compile-time buffer index so every LDS offset is
+  // an immediate on top of the per-lane offsets
+  auto step = [&](auto buf_tag, int t) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (t + 1 < nt) issue_tile(t + 1, BUF ^ 1);
+    const lds_char* kt = lds + BUF * C::TILE;
+    const lds_char* vt = lds + (2 + BUF) * C::TILE;
+    const int kfirst = uniform(sKp[BUF][0]);
+    const int klast = uniform(sKp[BUF][C::BN - 1]);
     if (wave_live && kfirst <= wqmax) {
-      const bool full = klast <= wqmin;
       f32x16 s[C::NKB];
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-        s[kb] = f32x16{};
-        const uint16_t* kr = &sK[buf][(kb * 32 + l32) * C::KSTR + 8 * hh];
+        const int rb = kb * 32 * D * 2;
+        s[kb] = mfma32x32x16(lds_read_b128(kt, rb + koff[0]), qf[0], f32x16{});
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 16 * ks));
-          s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
-        }
+        for (int ks = 1; ks < C::KS; ++ks)
+          s[kb] = mfma32x32x16(lds_read_b128(kt, rb + koff[ks]), qf[ks], s[kb]);
       }
-      if (!full) {
+      if (klast > wqmin) {  // tile straddles this wave's positions (or the tail)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (sKp[buf][key] > qpos) s[kb][i] = -INFINITY;
+            if (sKp[BUF][key] > qpos) s[kb][i] = -INFINITY;
           }
       }
       float mt = -INFINITY;
@@ -215,6 +179,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
       mt = max_halves(mt) * c;
       if (__ballot(mt > m_run + 8.0f)) {
+        asm volatile("" ::: "memory");
         const float m_new = fmaxf(m_run, mt);
         const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
 #pragma unroll
@@ -224,40 +189,53 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       }
       const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       uint32_t pk[C::NKB][8];
-      float psum = 0.f;
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const float e0 = fast_exp2(fmaf(s[kb][i], c, neg_m));
           const float e1 = fast_exp2(fmaf(s[kb][i + 1], c, neg_m));
-          psum += e0 + e1;
           pk[kb][i >> 1] = pack_bf16x2(e0, e1);
+          if (i & 2) ps1 += e0 + e1; else ps0 += e0 + e1;
         }
-      l_run += psum;
+      l_run += ps0 + ps1;
 #pragma unroll
       for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
         const int kb = ks2 >> 1, half = ks2 & 1;
         const u32x4 bw = {pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2],
                           pk[kb][4 * half + 3]};
         const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-        const uint16_t* vr = &sV[buf][l32 * C::VSTR + 16 * ks2 + 8 * hh];
+        const int rb = ks2 * 16 * D * 2;
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(vr + mb * 32 * C::VSTR));
-          oacc[mb] = mfma32x32x16(a, b, oacc[mb]);
-        }
+        for (int mb = 0; mb < C::MB; ++mb)
+          oacc[mb] = mfma32x32x16(lds_read_tr(vt, rb + voff[0][mb], rb + voff[1][mb]), b,
+                                  oacc[mb]);
       }
     }
-    if (t + 1 < nt) store_tile(buf ^ 1);
+    if (t + 1 < nt) {
+      if (tid < C::BN) sKp[BUF ^ 1][tid] = kpreg;
+      wait_vmem();
+    }
     __syncthreads();
+  };
+
+  if (nt > 0) {
+    issue_tile(0, 0);
+    if (tid < C::BN) sKp[0][tid] = kpreg;
+    wait_vmem();
+  }
+  __syncthreads();
+  for (int t = 0; t < nt; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nt) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   // ---- epilogue: normalise, then write or merge ----
   const float l_tot = sum_halves(l_run);
   if (!row_ok) return;
   const bool has = l_tot > 0.f;
-  const float inv = has ? 1.f / l_tot : 0.f;
+  const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
   const float lse2 = has ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;  // log2 domain
   float* orow = p.o + ((size_t)row * p.hq + h) * D;
   float* lrow = p.lse + (size_t)h * p.sq + row;
@@ -278,7 +256,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     const float mx = fmaxf(la2, lse2);
     const float ea = fast_exp2(la2 - mx), eb = fast_exp2(lse2 - mx);
     const float tot = ea + eb;
-    const float wa = ea / tot, wb = eb / tot * inv;
+    const float rt = __builtin_amdgcn_rcpf(tot);
+    const float wa = ea * rt, wb = eb * rt * inv;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -293,6 +272,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     if (hh == 0) *lrow = (mx + __builtin_amdgcn_logf(tot)) * kLn2;
   }
 }
+
+template __global__ void attn_fwd_kernel<64, false>(FwdParams);
+template __global__ void attn_fwd_kernel<64, true>(FwdParams);
+template __global__ void attn_fwd_kernel<128, false>(FwdParams);
+template __global__ void attn_fwd_kernel<128, true>(FwdParams);
 
 template <int D>
 hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {

@@ -5,13 +5,21 @@
 //   B (16 x 32, K x N): lane l supplies col n = l % 32, k = 8*(l/32) + 0..7
 //   C (32 x 32, fp32) : lane l holds col n = l % 32 and, for i = 0..15,
 //                       row m = 8*(i/4) + 4*(l/32) + (i%4)
-// Hence an accumulator row index r of lane-half hh = l/32 takes the values
-// {0,1,2,3, 8,9,10,11, 16..19, 24..27} (+4 for hh = 1).  When a C tile is fed
-// back as the B operand of the next contraction (K = its row index), the
-// first 8 accumulator entries form K-step 0 and the last 8 K-step 1, with
-// the row set of each lane-half acting as that half's k = 0..7.  The operand
-// paired with it must list its rows in the same order; kPerm16 below gives
-// the position of row r (0..15 within a K-step) in that order.
+// A C tile fed back as the B operand of the next contraction (its row index
+// becoming K) supplies, in K-step 0, rows {0-3, 8-11} from lane-half 0 and
+// rows {4-7, 12-15} from lane-half 1 (entries 0..7), and the same +16 in
+// K-step 1 (entries 8..15).  The paired A operand must list its K rows in
+// that order; the transposing LDS read below produces exactly that order.
+//
+// LDS tiles: rows of D bf16 (row-major, no padding) whose 16-byte chunks are
+// XOR-swizzled, chunk c of row r stored at chunk slot c ^ swz(r).  With
+// swz(r) = ((r & 3) << 2) | ((r >> 2) & 3) (D = 128) both access patterns used
+// here are free of bank conflicts: 16 lanes reading one chunk of 16
+// consecutive rows (ds_read_b128), and the transposing read of 4 rows x 4
+// chunks per 32 lanes (ds_read_b64_tr_b16).  Tiles are filled by direct
+// global->LDS loads (global_load_lds_dwordx4): lane l of a wave writes LDS
+// bytes [16 l, 16 l + 16) of the wave's 1 KiB window, so the swizzle is
+// applied by choosing which global chunk each lane fetches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,22 +35,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPosInf = 0x7fffffff;
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Position, within one K-step of 16 rows, at which row r is stored so that
-// lane-half 0 reads rows {0-3, 8-11} and lane-half 1 rows {4-7, 12-15} as 8
-// consecutive elements: quads 1 and 2 trade places.
-__device__ __forceinline__ constexpr int kPerm16(int r) {
-  const int quad = r >> 2;
-  const int q2 = (quad == 1) ? 2 : (quad == 2 ? 1 : quad);
-  return (q2 << 2) | (r & 3);
 }
 
 // Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
@@ -50,6 +54,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   bf16x2 b = __builtin_convertvector(v, bf16x2);
   return __builtin_bit_cast(uint32_t, b);
+}
+
+// acc + lo(w) + hi(w) for a packed bf16 pair (v_dot2c_f32_bf16 against 1.0)
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -67,6 +77,8 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Workgroup order that keeps consecutive logical tiles on one XCD: the
 // dispatcher deals workgroup b to XCD b % 8, so logical tile
 // (b % 8) * (n / 8) + b / 8 runs on XCD b % 8 and each XCD sweeps one
@@ -74,6 +86,100 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int xcd_logical_block(int b, int n) {
   if ((n & 7) != 0) return b;
   return (b & 7) * (n >> 3) + (b >> 3);
+}
+
+// ---- swizzled LDS tiles -----------------------------------------------------
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// byte offset of (row, 16-byte chunk c) in a swizzled tile of rows of D bf16
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int c) {
+  return row * (D * 2) + ((c ^ swz<D>(row)) << 4);
+}
+
+// Direct global->LDS fill of a ROWS x D bf16 tile by THREADS threads.
+// Tile row r lives at global element offset r * row_stride from `base`.
+// Per-lane byte offsets (loop invariant, from tile_src_offsets) are added to a
+// wave-uniform base, so the loads use the scalar-base + 32-bit-offset form.
+template <int D, int ROWS, int THREADS>
+struct TileLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int ROUNDS = ROWS * CPR / THREADS;
+  static_assert((ROWS * CPR) % THREADS == 0, "tile must be a whole number of load rounds");
+  uint32_t off[ROUNDS];   // byte offset of this lane's chunk, row 0 = tile row 0
+  int row[ROUNDS];        // tile row of this lane's chunk in each round
+  int wave_base;
+
+  __device__ __forceinline__ void init(int tid, size_t row_stride) {
+    wave_base = uniform((tid >> 6) << 6);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int c = 0; c < ROUNDS; ++c) {
+      const int slot = c * THREADS + wave_base + lane;
+      const int r = slot / CPR;
+      const int chunk = (slot % CPR) ^ swz<D>(r);
+      row[c] = r;
+      off[c] = (uint32_t)(((size_t)r * row_stride + chunk * 8) * 2);
+    }
+  }
+  // all rows of the tile exist: base points at tile row 0
+  __device__ __forceinline__ void load(lds_char* tile, const uint16_t* base) const {
+#pragma unroll
+    for (int c = 0; c < ROUNDS; ++c)
+      __builtin_amdgcn_global_load_lds((const char*)base + off[c],
+                                       (__attribute__((address_space(3))) void*)(
+                                           tile + (c * THREADS + wave_base) * 16),
+                                       16, 0, 0);
+  }
+  // tail tile: rows at or past `rows_left` re-read the last existing row
+  __device__ __forceinline__ void load_clamped(lds_char* tile, const uint16_t* base,
+                                               size_t row_stride, int rows_left) const {
+#pragma unroll
+    for (int c = 0; c < ROUNDS; ++c) {
+      const int back = row[c] - min(row[c], rows_left - 1);
+      const char* src = (const char*)base + off[c] - (size_t)back * row_stride * 2;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(
+                                                tile + (c * THREADS + wave_base) * 16),
+                                       16, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A operand rows = tile rows (k = head dim): lane reads chunk c of row r.
+__device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* tile, int off) {
+  return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4*)(tile + off));
+}
+
+// Transposing read: for a tile whose rows are the contraction index k and
+// whose columns are the MFMA row index m, returns the A operand (m = lane %
+// 32) for one 16-row K-step, rows in the order of the accumulator-as-B
+// convention above.  Within each 16-lane group, lane i receives element i%4
+// of the 8-byte piece addressed by lane 4e + i/4 as its element e; the
+// caller's per-lane byte offsets implement that pattern (see tr_offset).
+__device__ __forceinline__ bf16x8 lds_read_tr(const lds_char* tile, int off_lo, int off_hi) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_lo));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_hi));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  const u32x4 w = {ua[0], ua[1], ub[0], ub[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Per-lane byte offset of the transposing read covering tile rows
+// kbase + 16*ks + {4hh..4hh+3} (rh = 0) or + 8 + {..} (rh = 1) and head-dim
+// columns 32*mb + (lane % 32): lane (group g = lane/16, j = lane%16) points
+// at row ... + j/4, columns 32*mb + 16*(g%2) + 4*(j%4) .. +3.
+template <int D>
+__device__ __forceinline__ int tr_offset(int lane, int kbase, int rh, int mb) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = kbase + 8 * rh + 4 * (g >> 1) + (j >> 2);
+  const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
+  return row * (D * 2) + (((col >> 3) ^ swz<D>(row)) << 4) + ((col & 7) << 1);
 }
 
 }  // namespace mmsp

@@ -32,7 +32,7 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  int sq, sk, hq, hkv, group, n_ktiles;
+  int sq, sk, hq, hkv, group, n_ktiles, n_qtiles;
   float scale;
   float scale_log2;
   int causal, accumulate;
@@ -49,6 +49,7 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dout, int sq
                                  float* delta, float* dq_zero, hipStream_t stream);
 
 int bwd_keys_per_block();
+int bwd_rows_per_block();
 hipError_t launch_attn_bwd(const BwdParams& p, int d, hipStream_t stream);
 
 // shard balance: vis/owner scratch of n/g int32 each (MODALITY only)
