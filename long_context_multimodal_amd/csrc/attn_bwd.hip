@@ -51,12 +51,23 @@ struct DkdvCfg {
 template <int D>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   using C = DkdvCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * C::TILE + C::VTILE];  // Q0|Q1|dO0|dO1|V
+  // one LDS object per pipeline buffer (the compiler then knows the direct
+  // loads into one buffer never alias reads of the other)
+  __shared__ __attribute__((aligned(16))) char sQ0[C::TILE], sQ1[C::TILE];
+  __shared__ __attribute__((aligned(16))) char sO0[C::TILE], sO1[C::TILE];
+  __shared__ __attribute__((aligned(16))) char sVrows[C::VTILE];
   __shared__ __attribute__((aligned(16))) float sL[2][C::BQ];      // LSE*log2e (+inf empty)
   __shared__ __attribute__((aligned(16))) float sDl[2][C::BQ];     // delta
   __shared__ __attribute__((aligned(16))) int sQp[2][C::BQ];       // positions
   __shared__ int sQlast[2];
-  lds_char* lds = (lds_char*)smem;
+  auto qtile = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)sQ0; else return (lds_char*)sQ1;
+  };
+  auto otile = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)sO0; else return (lds_char*)sO1;
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,10 +123,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     TileLoader<D, C::BK, C::THREADS> vld;
     vld.init(tid, kv_stride);
     const uint16_t* vb = p.v + (size_t)j0 * kv_stride + (size_t)kvh * D;
-    if (j0 + C::BK <= p.sk) vld.load(lds + 4 * C::TILE, vb);
-    else vld.load_clamped(lds + 4 * C::TILE, vb, kv_stride, p.sk - j0);
+    if (j0 + C::BK <= p.sk) vld.load((lds_char*)sVrows, vb);
+    else vld.load_clamped((lds_char*)sVrows, vb, kv_stride, p.sk - j0);
   }
-  const lds_char* vrows = lds + 4 * C::TILE + uniform(wave * 32 * D * 2);
+  const lds_char* vrows = (lds_char*)sVrows + uniform(wave * 32 * D * 2);
 
   int qoff[C::KS];  // A = Q / dO rows: row l32, chunk 2 ks + hh
 #pragma unroll
@@ -137,16 +148,16 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     h = kvh * p.group + gi;
     q0 = (qt0 + it % per_head) * C::BQ;
   };
-  auto issue_tile = [&](int it, int buf) {
+  auto issue_tile = [&](int it, auto buf) {
     int h, q0;
     tile_of(it, h, q0);
     const size_t o = (size_t)q0 * q_row_stride + (size_t)h * D;
     if (q0 + C::BQ <= p.sq) {
-      ld.load(lds + buf * C::TILE, p.q + o);
-      ld.load(lds + (2 + buf) * C::TILE, p.dout + o);
+      ld.load(qtile(buf), p.q + o);
+      ld.load(otile(buf), p.dout + o);
     } else {
-      ld.load_clamped(lds + buf * C::TILE, p.q + o, q_row_stride, p.sq - q0);
-      ld.load_clamped(lds + (2 + buf) * C::TILE, p.dout + o, q_row_stride, p.sq - q0);
+      ld.load_clamped(qtile(buf), p.q + o, q_row_stride, p.sq - q0);
+      ld.load_clamped(otile(buf), p.dout + o, q_row_stride, p.sq - q0);
     }
     if (tid < C::BQ) {
       const int i = q0 + tid;
@@ -184,9 +195,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
 
   auto step = [&](auto buf_tag, int it) {
     constexpr int BUF = decltype(buf_tag)::value;
-    if (it + 1 < total) issue_tile(it + 1, BUF ^ 1);
-    const lds_char* qt = lds + BUF * C::TILE;
-    const lds_char* dt = lds + (2 + BUF) * C::TILE;
+    using Next = std::integral_constant<int, BUF ^ 1>;
+    if (it + 1 < total) issue_tile(it + 1, Next{});
+    const lds_char* qt = qtile(buf_tag);
+    const lds_char* dt = otile(buf_tag);
     const int qfirst = uniform(sQp[BUF][0]);
     const int qlast = uniform(sQlast[BUF]);
     if (wave_live && qlast >= wkmin) {
@@ -251,14 +263,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   };
 
   if (total > 0) {
-    issue_tile(0, 0);
+    issue_tile(0, B0{});
     publish_tile(0);
   }
   wait_vmem();
   __syncthreads();
   for (int it = 0; it < total; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < total) step(std::integral_constant<int, 1>{}, it + 1);
+    step(B0{}, it);
+    if (it + 1 < total) step(B1{}, it + 1);
   }
 
   // ---- epilogue: dK = scale * (dK^T)^T, dV = (dV^T)^T ----
@@ -298,9 +310,20 @@ struct DqCfg {
 template <int D>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * C::TILE];  // [K0|K1|V0|V1]
-  __shared__ int sKp[2][C::BN];
-  lds_char* lds = (lds_char*)smem;
+  __shared__ __attribute__((aligned(16))) char sK0[C::TILE], sK1[C::TILE];
+  __shared__ __attribute__((aligned(16))) char sV0[C::TILE], sV1[C::TILE];
+  __shared__ int sKp0[C::BN], sKp1[C::BN];
+  auto ktile = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)sK0; else return (lds_char*)sK1;
+  };
+  auto vtile = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)sV0; else return (lds_char*)sV1;
+  };
+  auto kpos_of = [&](auto b) -> int* {
+    if constexpr (decltype(b)::value == 0) return sKp0; else return sKp1;
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -377,15 +400,15 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   TileLoader<D, C::BN, C::THREADS> ld;
   ld.init(tid, kv_row_stride);
   int kpreg = kPosInf;
-  auto issue_tile = [&](int t, int buf) {
+  auto issue_tile = [&](int t, auto buf) {
     const int j0 = t * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
     if (j0 + C::BN <= p.sk) {
-      ld.load(lds + buf * C::TILE, kbase + o);
-      ld.load(lds + (2 + buf) * C::TILE, vbase + o);
+      ld.load(ktile(buf), kbase + o);
+      ld.load(vtile(buf), vbase + o);
     } else {
-      ld.load_clamped(lds + buf * C::TILE, kbase + o, kv_row_stride, p.sk - j0);
-      ld.load_clamped(lds + (2 + buf) * C::TILE, vbase + o, kv_row_stride, p.sk - j0);
+      ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, p.sk - j0);
+      ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, p.sk - j0);
     }
     if (tid < C::BN) {
       const int j = j0 + tid;
@@ -400,11 +423,13 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
 
   auto step = [&](auto buf_tag, int t) {
     constexpr int BUF = decltype(buf_tag)::value;
-    if (t + 1 < nt) issue_tile(t + 1, BUF ^ 1);
-    const lds_char* kt = lds + BUF * C::TILE;
-    const lds_char* vt = lds + (2 + BUF) * C::TILE;
-    const int kfirst = uniform(sKp[BUF][0]);
-    const int klast = uniform(sKp[BUF][C::BN - 1]);
+    using Next = std::integral_constant<int, BUF ^ 1>;
+    if (t + 1 < nt) issue_tile(t + 1, Next{});
+    const lds_char* kt = ktile(buf_tag);
+    const lds_char* vt = vtile(buf_tag);
+    const int* kp = kpos_of(buf_tag);
+    const int kfirst = uniform(kp[0]);
+    const int klast = uniform(kp[C::BN - 1]);
     if (wave_live && kfirst <= wqmax) {
       const bool straddle = klast > wqmin;
 #pragma unroll
@@ -422,7 +447,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (sKp[BUF][key] > qpos) s[i] = -INFINITY;
+            if (kp[key] > qpos) s[i] = -INFINITY;
           }
         }
         uint32_t dsk[8];
@@ -446,21 +471,21 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
       }
     }
     if (t + 1 < nt) {
-      if (tid < C::BN) sKp[BUF ^ 1][tid] = kpreg;
+      if (tid < C::BN) kpos_of(Next{})[tid] = kpreg;
       wait_vmem();
     }
     __syncthreads();
   };
 
   if (nt > 0) {
-    issue_tile(0, 0);
-    if (tid < C::BN) sKp[0][tid] = kpreg;
+    issue_tile(0, B0{});
+    if (tid < C::BN) sKp0[tid] = kpreg;
     wait_vmem();
   }
   __syncthreads();
   for (int t = 0; t < nt; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nt) step(std::integral_constant<int, 1>{}, t + 1);
+    step(B0{}, t);
+    if (t + 1 < nt) step(B1{}, t + 1);
   }
 
   // ---- epilogue: dq_acc += scale * (dQ^T)^T (this lane owns its elements) ----

@@ -48,9 +48,22 @@ struct FwdCfg {
 template <int D, bool ACC>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * C::TILE];
-  __shared__ int sKp[2][C::BN];
-  lds_char* lds = (lds_char*)smem;  // [K0 | K1 | V0 | V1]
+  // one LDS object per pipeline buffer, so the compiler can tell that the
+  // direct loads into one buffer never alias reads of the other
+  __shared__ __attribute__((aligned(16))) char sK0[C::TILE], sK1[C::TILE];
+  __shared__ __attribute__((aligned(16))) char sV0[C::TILE], sV1[C::TILE];
+  __shared__ int sKp0[C::BN], sKp1[C::BN];
+  auto ktile = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)sK0; else return (lds_char*)sK1;
+  };
+  auto vtile = [&](auto b) -> lds_char* {
+    if constexpr (decltype(b)::value == 0) return (lds_char*)sV0; else return (lds_char*)sV1;
+  };
+  auto kpos_of = [&](auto b) -> int* {
+    if constexpr (decltype(b)::value == 0) return sKp0; else return sKp1;
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,15 +133,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   TileLoader<D, C::BN, C::THREADS> ld;
   ld.init(tid, kv_row_stride);
   int kpreg = kPosInf;
-  auto issue_tile = [&](int t, int buf) {
+  auto issue_tile = [&](int t, auto buf) {
     const int j0 = t * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
     if (j0 + C::BN <= p.sk) {
-      ld.load(lds + buf * C::TILE, kbase + o);
-      ld.load(lds + (2 + buf) * C::TILE, vbase + o);
+      ld.load(ktile(buf), kbase + o);
+      ld.load(vtile(buf), vbase + o);
     } else {
-      ld.load_clamped(lds + buf * C::TILE, kbase + o, kv_row_stride, p.sk - j0);
-      ld.load_clamped(lds + (2 + buf) * C::TILE, vbase + o, kv_row_stride, p.sk - j0);
+      ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, p.sk - j0);
+      ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, p.sk - j0);
     }
     if (tid < C::BN) {
       const int j = j0 + tid;
@@ -147,11 +160,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   // an immediate on top of the per-lane offsets
   auto step = [&](auto buf_tag, int t) {
     constexpr int BUF = decltype(buf_tag)::value;
-    if (t + 1 < nt) issue_tile(t + 1, BUF ^ 1);
-    const lds_char* kt = lds + BUF * C::TILE;
-    const lds_char* vt = lds + (2 + BUF) * C::TILE;
-    const int kfirst = uniform(sKp[BUF][0]);
-    const int klast = uniform(sKp[BUF][C::BN - 1]);
+    using Next = std::integral_constant<int, BUF ^ 1>;
+    if (t + 1 < nt) issue_tile(t + 1, Next{});
+    const lds_char* kt = ktile(buf_tag);
+    const lds_char* vt = vtile(buf_tag);
+    const int* kp = kpos_of(buf_tag);
+    const int kfirst = uniform(kp[0]);
+    const int klast = uniform(kp[C::BN - 1]);
     if (wave_live && kfirst <= wqmax) {
       f32x16 s[C::NKB];
 #pragma unroll
@@ -169,7 +184,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (sKp[BUF][key] > qpos) s[kb][i] = -INFINITY;
+            if (kp[key] > qpos) s[kb][i] = -INFINITY;
           }
       }
       float mt = -INFINITY;
@@ -214,21 +229,21 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       }
     }
     if (t + 1 < nt) {
-      if (tid < C::BN) sKp[BUF ^ 1][tid] = kpreg;
+      if (tid < C::BN) kpos_of(Next{})[tid] = kpreg;
       wait_vmem();
     }
     __syncthreads();
   };
 
   if (nt > 0) {
-    issue_tile(0, 0);
-    if (tid < C::BN) sKp[0][tid] = kpreg;
+    issue_tile(0, B0{});
+    if (tid < C::BN) sKp0[tid] = kpreg;
     wait_vmem();
   }
   __syncthreads();
   for (int t = 0; t < nt; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nt) step(std::integral_constant<int, 1>{}, t + 1);
+    step(B0{}, t);
+    if (t + 1 < nt) step(B1{}, t + 1);
   }
 
   // ---- epilogue: normalise, then write or merge ----
