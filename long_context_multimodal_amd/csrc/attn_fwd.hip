@@ -8,10 +8,14 @@
 // over ring steps).  The accumulation is done exactly with the chunk's
 // log-sum-exp (MMSP_ACCUMULATE merges in the epilogue).
 //
-// Design (one workgroup = 128 query rows of one query head, 4 waves):
-//  * each wave owns 32 query rows; Q stays in registers for the whole loop;
-//  * K/V tiles of 64 keys go straight from HBM to a double-buffered,
-//    XOR-swizzled LDS area with 16-byte direct loads (no staging registers);
+// Design (one workgroup = 256 query rows of one query head, 8 waves, two
+// waves per SIMD):
+//  * each wave owns 32 query rows; Q stays in registers; the 8 waves share
+//    every K/V tile, so each tile crosses HBM/L2 -> LDS once per 256 rows;
+//  * K/V tiles of 64 keys go straight from HBM to a 3-stage, XOR-swizzled
+//    LDS ring with 16-byte direct loads (no staging registers); each stage
+//    is its own LDS object so loads into one never stall reads of another;
+//    the key positions of a tile are loaded directly into a per-wave slot;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a lane holds 16 scores of ONE
 //    query, so the row max/sum are in-lane plus one permlane32 swap;
 //  * O^T += V^T P^T: the score registers, converted to bf16, are the B
@@ -23,7 +27,7 @@
 //    row sums stay in fp32 (exact LSE for the merge and the backward);
 //  * causal tile skipping from the sorted positions: a binary search bounds
 //    the key range of the workgroup, each wave skips tiles it cannot see and
-//    masks only the tiles that straddle its rows' positions;
+//    masks only the tiles that straddle its rows' positions (or the tail);
 //  * GQA: query head h reads KV head h / G; the workgroup order keeps the
 //    query heads of one KV head on one XCD (shared L2).
 #include <type_traits>
@@ -36,34 +40,49 @@ namespace {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;
-  static constexpr int BN = 64;
-  static constexpr int THREADS = 256;
-  static constexpr int KS = D / 16;        // K-steps of S^T = K Q^T
-  static constexpr int MB = D / 32;        // 32-row blocks of O^T
-  static constexpr int NKB = BN / 32;      // 32-key blocks per tile
-  static constexpr int TILE = BN * D * 2;  // bytes of one K or V tile
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 512;
+  static constexpr int QB = 1;                // 32-row query blocks per wave
+  static constexpr int BM = WAVES * 32 * QB;  // query rows per workgroup
+  static constexpr int BN = 64;               // keys per tile
+  static constexpr int NS = 3;                // pipeline stages
+  static constexpr int KS = D / 16;           // K-steps of S^T = K Q^T
+  static constexpr int MB = D / 32;           // 32-row blocks of O^T
+  static constexpr int NKB = BN / 32;         // 32-key blocks per tile
+  static constexpr int TILE = BN * D * 2;     // bytes of one K or V tile
+  using Loader = TileLoader<D, BN, THREADS>;
+  static constexpr int VMEM = 2 * Loader::ROUNDS + 1;  // vector-memory ops per tile per thread
 };
 
 template <int D, bool ACC>
-__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
+__global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  // one LDS object per pipeline buffer, so the compiler can tell that the
-  // direct loads into one buffer never alias reads of the other
-  __shared__ __attribute__((aligned(16))) char sK0[C::TILE], sK1[C::TILE];
-  __shared__ __attribute__((aligned(16))) char sV0[C::TILE], sV1[C::TILE];
-  __shared__ int sKp0[C::BN], sKp1[C::BN];
+  // one LDS object per pipeline stage
+  __shared__ __attribute__((aligned(16))) char sK0[C::TILE], sK1[C::TILE], sK2[C::TILE];
+  __shared__ __attribute__((aligned(16))) char sV0[C::TILE], sV1[C::TILE], sV2[C::TILE];
+  __shared__ __attribute__((aligned(16))) int sP0[C::WAVES * C::BN], sP1[C::WAVES * C::BN],
+      sP2[C::WAVES * C::BN];
   auto ktile = [&](auto b) -> lds_char* {
-    if constexpr (decltype(b)::value == 0) return (lds_char*)sK0; else return (lds_char*)sK1;
+    constexpr int S = decltype(b)::value;
+    if constexpr (S == 0) return (lds_char*)sK0;
+    else if constexpr (S == 1) return (lds_char*)sK1;
+    else return (lds_char*)sK2;
   };
   auto vtile = [&](auto b) -> lds_char* {
-    if constexpr (decltype(b)::value == 0) return (lds_char*)sV0; else return (lds_char*)sV1;
+    constexpr int S = decltype(b)::value;
+    if constexpr (S == 0) return (lds_char*)sV0;
+    else if constexpr (S == 1) return (lds_char*)sV1;
+    else return (lds_char*)sV2;
   };
-  auto kpos_of = [&](auto b) -> int* {
-    if constexpr (decltype(b)::value == 0) return sKp0; else return sKp1;
+  auto ptile = [&](auto b) -> int* {
+    constexpr int S = decltype(b)::value;
+    if constexpr (S == 0) return sP0;
+    else if constexpr (S == 1) return sP1;
+    else return sP2;
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,22 +95,24 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   const int qt = p.n_qtiles - 1 - (logical % p.n_qtiles);  // late (heavier) tiles first
   const int kvh = h / p.group;
   const int q0 = qt * C::BM;
-  const int row = q0 + wave * 32 + l32;
-  const bool row_ok = row < p.sq;
+  const int wr0 = q0 + wave * 32 * C::QB;  // first row of this wave
 
-  // ---- positions of this lane, this wave and this workgroup ----
-  int qpos = INT_MIN;
-  if (row_ok) qpos = p.causal ? p.q_pos[row] : (kPosInf - 1);
-  const int wr0 = q0 + wave * 32;
-  const bool wave_live = wr0 < p.sq;
-  int wqmin = 0, wqmax = INT_MIN;
-  if (wave_live) {
-    const int wlast = min(wr0 + 31, p.sq - 1);
-    wqmin = p.causal ? p.q_pos[wr0] : (kPosInf - 1);
-    wqmax = p.causal ? p.q_pos[wlast] : (kPosInf - 1);
+  // ---- positions: per lane and block, per block range, workgroup range ----
+  int row[C::QB], qpos[C::QB], bmin[C::QB];
+  bool row_ok[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    row[qb] = wr0 + 32 * qb + l32;
+    row_ok[qb] = row[qb] < p.sq;
+    qpos[qb] = INT_MIN;
+    if (row_ok[qb]) qpos[qb] = p.causal ? p.q_pos[row[qb]] : (kPosInf - 1);
+    const int r0 = wr0 + 32 * qb;
+    bmin[qb] = uniform(r0 < p.sq ? (p.causal ? p.q_pos[r0] : (kPosInf - 1)) : kPosInf);
   }
-  wqmin = uniform(wqmin);
-  wqmax = uniform(wqmax);
+  const bool wave_live = wr0 < p.sq;
+  const int wqmax =
+      uniform(wave_live ? (p.causal ? p.q_pos[min(wr0 + 32 * C::QB - 1, p.sq - 1)] : kPosInf - 1)
+                        : INT_MIN);
   int nk = p.sk;
   if (p.causal) {
     const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
@@ -104,15 +125,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   }
   const int nt = uniform((nk + C::BN - 1) / C::BN);
 
-  // ---- Q fragment: B operand of S^T = K Q^T (col = query, k = head dim) ----
-  bf16x8 qf[C::KS];
-  {
-    const uint16_t* qp = p.q + ((size_t)row * p.hq + h) * D + 8 * hh;
+  // ---- Q fragments: B operands of S^T = K Q^T (col = query, k = head dim) ----
+  bf16x8 qf[C::QB][C::KS];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const uint16_t* qp = p.q + ((size_t)row[qb] * p.hq + h) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (row_ok) w = *(const u32x4*)(qp + 16 * ks);
-      qf[ks] = __builtin_bit_cast(bf16x8, w);
+      if (row_ok[qb]) w = *(const u32x4*)(qp + 16 * ks);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -130,161 +152,179 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   const size_t kv_row_stride = (size_t)p.hkv * D;
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
-  TileLoader<D, C::BN, C::THREADS> ld;
+  // without a causal mask positions are unused; any readable int array will do
+  const int32_t* pos_src = p.causal ? p.k_pos : (const int32_t*)p.k;
+  typename C::Loader ld;
   ld.init(tid, kv_row_stride);
-  int kpreg = kPosInf;
-  auto issue_tile = [&](int t, auto buf) {
+  auto issue_tile = [&](int t, auto stage) {
     const int j0 = t * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
     if (j0 + C::BN <= p.sk) {
-      ld.load(ktile(buf), kbase + o);
-      ld.load(vtile(buf), vbase + o);
+      ld.load(ktile(stage), kbase + o);
+      ld.load(vtile(stage), vbase + o);
     } else {
-      ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, p.sk - j0);
-      ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, p.sk - j0);
+      ld.load_clamped(ktile(stage), kbase + o, kv_row_stride, p.sk - j0);
+      ld.load_clamped(vtile(stage), vbase + o, kv_row_stride, p.sk - j0);
     }
-    if (tid < C::BN) {
-      const int j = j0 + tid;
-      kpreg = (j < p.sk) ? (p.causal ? p.k_pos[j] : 0) : kPosInf;
-    }
+    pos_load_direct((lds_char*)(ptile(stage) + wave * C::BN), pos_src, j0,
+                    min(C::BN, p.sk - j0));
   };
 
-  f32x16 oacc[C::MB];
+  f32x16 oacc[C::QB][C::MB];
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) oacc[mb] = f32x16{};
-  float m_run = -INFINITY;  // running max, log2 domain
-  float l_run = 0.f;        // this lane's partial row sum
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) oacc[qb][mb] = f32x16{};
+  float m_run[C::QB], l_run[C::QB];  // running max (log2 domain), lane's partial row sum
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
   const float c = p.scale_log2;
+  const bool causal = p.causal != 0;
 
-  // one K/V tile; BUF is a compile-time buffer index so every LDS offset is
-  // an immediate on top of the per-lane offsets
-  auto step = [&](auto buf_tag, int t) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    using Next = std::integral_constant<int, BUF ^ 1>;
-    if (t + 1 < nt) issue_tile(t + 1, Next{});
-    const lds_char* kt = ktile(buf_tag);
-    const lds_char* vt = vtile(buf_tag);
-    const int* kp = kpos_of(buf_tag);
+  // one K/V tile; STAGE is compile-time so every LDS object and offset is fixed
+  auto step = [&](auto stage, int t) {
+    constexpr int ST = decltype(stage)::value;
+    using Ahead = std::integral_constant<int, (ST + 2) % 3>;
+    if (t + 1 < nt) wait_vmem_le<C::VMEM>(); else wait_vmem_le<0>();
+    barrier_only();  // tile t visible to all waves; stage of tile t-1 free
+    if (t + 2 < nt) issue_tile(t + 2, Ahead{});
+    const lds_char* kt = ktile(stage);
+    const lds_char* vt = vtile(stage);
+    const int* kp = ptile(stage) + wave * C::BN;
     const int kfirst = uniform(kp[0]);
     const int klast = uniform(kp[C::BN - 1]);
-    if (wave_live && kfirst <= wqmax) {
-      f32x16 s[C::NKB];
+    const int valid = min(C::BN, p.sk - t * C::BN);
+    const bool tail = valid < C::BN;
+    if (!wave_live || (causal && kfirst > wqmax)) return;
+
+    f32x16 s[C::QB][C::NKB];
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        const int rb = kb * 32 * D * 2;
-        s[kb] = mfma32x32x16(lds_read_b128(kt, rb + koff[0]), qf[0], f32x16{});
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      const int rb = kb * 32 * D * 2;
+      bf16x8 a = lds_read_b128(kt, rb + koff[0]);
 #pragma unroll
-        for (int ks = 1; ks < C::KS; ++ks)
-          s[kb] = mfma32x32x16(lds_read_b128(kt, rb + koff[ks]), qf[ks], s[kb]);
+      for (int qb = 0; qb < C::QB; ++qb) s[qb][kb] = mfma32x32x16(a, qf[qb][0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < C::KS; ++ks) {
+        a = lds_read_b128(kt, rb + koff[ks]);
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) s[qb][kb] = mfma32x32x16(a, qf[qb][ks], s[qb][kb]);
       }
-      if (klast > wqmin) {  // tile straddles this wave's positions (or the tail)
+    }
+
+    uint32_t pk[C::QB][C::NKB][8];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      if (tail || (causal && klast > bmin[qb])) {  // straddles this block's positions
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (kp[key] > qpos) s[kb][i] = -INFINITY;
+            const bool hide = (key >= valid) | (causal & (kp[key] > qpos[qb]));
+            s[qb][kb][i] = hide ? -INFINITY : s[qb][kb][i];
           }
       }
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[qb][kb][i]);
       mt = max_halves(mt) * c;
-      if (__ballot(mt > m_run + 8.0f)) {
+      if (__ballot(mt > m_run[qb] + 8.0f)) {
         asm volatile("" ::: "memory");
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[qb] - m_new);
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) oacc[mb] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
+        for (int mb = 0; mb < C::MB; ++mb) oacc[qb][mb] *= alpha;
+        l_run[qb] *= alpha;
+        m_run[qb] = m_new;
       }
-      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-      uint32_t pk[C::NKB][8];
+      const float neg_m = (m_run[qb] == -INFINITY) ? 0.f : -m_run[qb];
       float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float e0 = fast_exp2(fmaf(s[kb][i], c, neg_m));
-          const float e1 = fast_exp2(fmaf(s[kb][i + 1], c, neg_m));
-          pk[kb][i >> 1] = pack_bf16x2(e0, e1);
+          const float e0 = fast_exp2(fmaf(s[qb][kb][i], c, neg_m));
+          const float e1 = fast_exp2(fmaf(s[qb][kb][i + 1], c, neg_m));
+          pk[qb][kb][i >> 1] = pack_bf16x2(e0, e1);
           if (i & 2) ps1 += e0 + e1; else ps0 += e0 + e1;
         }
-      l_run += ps0 + ps1;
+      l_run[qb] += ps0 + ps1;
+    }
+
 #pragma unroll
-      for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
-        const int kb = ks2 >> 1, half = ks2 & 1;
-        const u32x4 bw = {pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2],
-                          pk[kb][4 * half + 3]};
-        const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-        const int rb = ks2 * 16 * D * 2;
+    for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
+      const int kb = ks2 >> 1, half = ks2 & 1;
+      const int rb = ks2 * 16 * D * 2;
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-          oacc[mb] = mfma32x32x16(lds_read_tr(vt, rb + voff[0][mb], rb + voff[1][mb]), b,
-                                  oacc[mb]);
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const bf16x8 a = lds_read_tr(vt, rb + voff[0][mb], rb + voff[1][mb]);
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) {
+          const u32x4 bw = {pk[qb][kb][4 * half], pk[qb][kb][4 * half + 1],
+                            pk[qb][kb][4 * half + 2], pk[qb][kb][4 * half + 3]};
+          oacc[qb][mb] = mfma32x32x16(a, __builtin_bit_cast(bf16x8, bw), oacc[qb][mb]);
+        }
       }
     }
-    if (t + 1 < nt) {
-      if (tid < C::BN) kpos_of(Next{})[tid] = kpreg;
-      wait_vmem();
-    }
-    __syncthreads();
   };
 
-  if (nt > 0) {
-    issue_tile(0, B0{});
-    if (tid < C::BN) sKp0[tid] = kpreg;
-    wait_vmem();
-  }
-  __syncthreads();
-  for (int t = 0; t < nt; t += 2) {
-    step(B0{}, t);
-    if (t + 1 < nt) step(B1{}, t + 1);
+  if (nt > 0) issue_tile(0, S0{});
+  if (nt > 1) issue_tile(1, S1{});
+  for (int t = 0; t < nt; t += 3) {
+    step(S0{}, t);
+    if (t + 1 < nt) step(S1{}, t + 1);
+    if (t + 2 < nt) step(S2{}, t + 2);
   }
 
   // ---- epilogue: normalise, then write or merge ----
-  const float l_tot = sum_halves(l_run);
-  if (!row_ok) return;
-  const bool has = l_tot > 0.f;
-  const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-  const float lse2 = has ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;  // log2 domain
-  float* orow = p.o + ((size_t)row * p.hq + h) * D;
-  float* lrow = p.lse + (size_t)h * p.sq + row;
-  if (!ACC) {
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const float l_tot = sum_halves(l_run[qb]);
+    if (!row_ok[qb]) continue;
+    const bool has = l_tot > 0.f;
+    const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    const float lse2 = has ? m_run[qb] + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    float* orow = p.o + ((size_t)row[qb] * p.hq + h) * D;
+    float* lrow = p.lse + (size_t)h * p.sq + row[qb];
+    if (!ACC) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = mb * 32 + 8 * g + 4 * hh;
-        f32x4 val = {oacc[mb][4 * g] * inv, oacc[mb][4 * g + 1] * inv,
-                     oacc[mb][4 * g + 2] * inv, oacc[mb][4 * g + 3] * inv};
-        *(f32x4*)(orow + d0) = val;
-      }
-    if (hh == 0) *lrow = has ? lse2 * kLn2 : -INFINITY;
-  } else {
-    if (!has) return;  // merging with an empty result is the identity
-    const float la2 = *lrow * kLog2e;  // -inf stays -inf
-    const float mx = fmaxf(la2, lse2);
-    const float ea = fast_exp2(la2 - mx), eb = fast_exp2(lse2 - mx);
-    const float tot = ea + eb;
-    const float rt = __builtin_amdgcn_rcpf(tot);
-    const float wa = ea * rt, wb = eb * rt * inv;
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = mb * 32 + 8 * g + 4 * hh;
+          f32x4 val = {oacc[qb][mb][4 * g] * inv, oacc[qb][mb][4 * g + 1] * inv,
+                       oacc[qb][mb][4 * g + 2] * inv, oacc[qb][mb][4 * g + 3] * inv};
+          *(f32x4*)(orow + d0) = val;
+        }
+      if (hh == 0) *lrow = has ? lse2 * kLn2 : -INFINITY;
+    } else {
+      if (!has) continue;  // merging with an empty result is the identity
+      const float la2 = *lrow * kLog2e;  // -inf stays -inf
+      const float mx = fmaxf(la2, lse2);
+      const float ea = fast_exp2(la2 - mx), eb = fast_exp2(lse2 - mx);
+      const float tot = ea + eb;
+      const float rt = __builtin_amdgcn_rcpf(tot);
+      const float wa = ea * rt, wb = eb * rt * inv;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = mb * 32 + 8 * g + 4 * hh;
-        const f32x4 old = *(const f32x4*)(orow + d0);
-        f32x4 val;
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = fmaf(wa, old[e], wb * oacc[mb][4 * g + e]);
-        *(f32x4*)(orow + d0) = val;
-      }
-    if (hh == 0) *lrow = (mx + __builtin_amdgcn_logf(tot)) * kLn2;
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = mb * 32 + 8 * g + 4 * hh;
+          const f32x4 old = *(const f32x4*)(orow + d0);
+          f32x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = fmaf(wa, old[e], wb * oacc[qb][mb][4 * g + e]);
+          *(f32x4*)(orow + d0) = val;
+        }
+      if (hh == 0) *lrow = (mx + __builtin_amdgcn_logf(tot)) * kLn2;
+    }
   }
 }
 
@@ -297,9 +337,11 @@ template <int D>
 hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
   const int grid = p.n_qtiles * p.hq;
   if (p.accumulate)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, true>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, true>), dim3(grid), dim3(FwdCfg<D>::THREADS), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, false>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, false>), dim3(grid), dim3(FwdCfg<D>::THREADS), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

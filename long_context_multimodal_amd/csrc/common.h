@@ -151,6 +151,32 @@ struct TileLoader {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier without the memory fence of __syncthreads(): callers make
+// their own LDS traffic visible first (wait_vmem_le for direct loads,
+// lgkmcnt for ds writes), so in-flight prefetches of later tiles stay in flight.
+__device__ __forceinline__ void barrier_only() { __builtin_amdgcn_s_barrier(); }
+
+__device__ __forceinline__ void wait_lds_writes() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 64 key positions of a tile straight into this wave's LDS slot (lane l ->
+// slot[l]); rows at or past `valid` re-read the last existing position (the
+// caller masks them by index).
+__device__ __forceinline__ void pos_load_direct(lds_char* slot, const int32_t* src, int j0,
+                                                int valid) {
+  const int l = threadIdx.x & 63;
+  __builtin_amdgcn_global_load_lds(src + j0 + min(l, valid - 1),
+                                   (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
+}
+
 // A operand rows = tile rows (k = head dim): lane reads chunk c of row r.
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* tile, int off) {
   return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4*)(tile + off));
