@@ -198,6 +198,8 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--unfused", action="store_true", help="separate merge pass per chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring (one rank); --gpus {args.gpus} is "
@@ -208,6 +210,15 @@ def main():
     from long_context_multimodal_amd import mmsp, ring
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = 1 << 30  # bytes read and written once per copy
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+        return
     mmsp.lib()
     device = torch.device("cuda:0")
     w = WORKLOADS[args.workload]

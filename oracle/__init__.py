@@ -38,7 +38,7 @@ Modules:
 
 from .attention import attention_forward, visible_pairs  # noqa: F401
 from .merge import lse_merge, ring_forward  # noqa: F401
-from .backward import attention_backward, bwd_delta  # noqa: F401
+from .backward import attention_backward, attention_backward_magnitudes, bwd_delta  # noqa: F401
 from .balance import (  # noqa: F401
     zigzag_perm,
     modality_perm,

@@ -82,3 +82,58 @@ def attention_backward(q, k, v, do, lse, delta, q_pos, k_pos, scale=None):
             dq[r, h, :] += scale * (ds @ kh[cols])
             dk[cols, kv, :] += scale * (ds.T @ q[r, h, :])
     return dq, dk, dv
+
+
+def attention_backward_magnitudes(q, k, v, do, o, lse, q_pos, k_pos, scale=None):
+    """Sums of absolute terms of each gradient element of one chunk.
+
+    A backward that rounds P and dS to a format with unit roundoff u (and
+    takes delta from a rounded O) errs on each element by at most about
+    u times these sums:
+
+        Mv_j  = sum_i P_ij |dO_i|
+        Mq_i  = scale * sum_j (|dS_ij| + P_ij A_i) |k_j|
+        Mk_j  = scale * sum_i (|dS_ij| + P_ij A_i) |q_i|,   A_i = sum_c |dO_ic O_ic|
+
+    (elementwise absolute values; same layouts as :func:`attention_backward`).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    sq, hq, d = q.shape
+    sk, hkv, _ = k.shape
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    delta = bwd_delta(o, do)
+    absd = np.einsum("ihc,ihc->hi", np.abs(do), np.abs(o))
+    mq = np.zeros_like(q)
+    mk = np.zeros_like(k)
+    mv = np.zeros_like(v)
+    for h in range(hq):
+        kv = h // group
+        kh = k[:, kv, :]
+        vh = v[:, kv, :]
+        for b0 in range(0, sq, _ROWS):
+            r = slice(b0, min(b0 + _ROWS, sq))
+            qp = q_pos[r]
+            cols = np.nonzero(k_pos <= qp.max())[0]
+            if cols.size == 0:
+                continue
+            vis = k_pos[cols][None, :] <= qp[:, None]
+            l_r = lse[h, r]
+            live = np.isfinite(l_r)
+            s = (q[r, h, :] @ kh[cols].T) * scale
+            p = np.where(vis & live[:, None],
+                         np.exp(s - np.where(live, l_r, 0.0)[:, None]), 0.0)
+            dp = do[r, h, :] @ vh[cols].T
+            w = np.abs(p * (dp - delta[h, r][:, None])) + p * absd[h, r][:, None]
+            mv[cols, kv, :] += p.T @ np.abs(do[r, h, :])
+            mq[r, h, :] += scale * (w @ np.abs(kh[cols]))
+            mk[cols, kv, :] += scale * (w.T @ np.abs(q[r, h, :]))
+    return mq, mk, mv

@@ -1,0 +1,150 @@
+"""GPU parity at the full per-rank workload sizes, in the launch configuration
+bench.py times (GPU shard balance -> fused ring forward -> backward).
+
+The oracle cannot redo whole 8K x 64K attentions in seconds, so outputs are
+compared on sampled query rows (all heads; rows at tile, half and block
+boundaries plus seeded random rows), on one whole head for the backward, and
+through identities that hold at any size:
+  sum over all keys of all chunks of dK = 0 (softmax shift invariance) and
+  sum over all keys of dV = sum of dO over rows that see any key.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_multimodal_amd.workloads import GQA, MODALITY, RANK_FWD, TRAIN
+from tests.helpers import assert_close_abs, assert_close_rms, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from long_context_multimodal_amd import mmsp, ring
+    mmsp.lib()
+    return mmsp, ring
+
+
+def _dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _sample_rows(n, extra_edges=(), seed=0, n_random=16):
+    rows = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, n // 2 - 1, n // 2, n // 2 + 1, n - 1}
+    rows |= {e for e in extra_edges if 0 <= e < n}
+    rng = np.random.default_rng(seed)
+    rows |= set(rng.choice(n, n_random, replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _run(mm, w, backward=False, rank=0):
+    """Run the hot path on the GPU; return host copies and the oracle inputs."""
+    mmsp, ring = mm
+    import torch
+    qb, qv = w.q()
+    kb, kv = w.k()
+    vb, vv = w.v()
+    labels = w.labels()
+    mode = mmsp.BALANCE_MODALITY if w.layout == "modality" else mmsp.BALANCE_ZIGZAG
+    perm, _ = mmsp.shard_balance(w.n_tokens, w.n_ranks, mode, w.granularity,
+                                 labels=torch.from_numpy(labels).cuda()
+                                 if mode == mmsp.BALANCE_MODALITY else None,
+                                 with_inverse=False)
+    perm_np = to_np(perm).astype(np.int64)
+    want_perm = (oracle.modality_perm(labels, w.n_ranks, w.granularity)
+                 if mode == mmsp.BALANCE_MODALITY else oracle.zigzag_perm(w.n_tokens, w.n_ranks))
+    assert np.array_equal(perm_np, want_perm)  # bit-exact shard permutation
+    qp = perm[rank * w.shard:(rank + 1) * w.shard]
+    kps = [perm[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
+    q = _dev_bf16(qb)
+    ks = [_dev_bf16(kb[c]) for c in range(w.n_chunks)]
+    vs = [_dev_bf16(vb[c]) for c in range(w.n_chunks)]
+    o, lse, o16 = ring.ring_forward(q, ks, vs, qp, kps, rank=rank)
+    out = {"o": to_np(o), "lse": to_np(lse)}
+    gv = None
+    if backward:
+        gb, gv = w.do()
+        dq, dks, dvs = ring.ring_backward(q, ks, vs, _dev_bf16(gb), o16, lse, qp, kps, rank=rank)
+        out["dq"] = to_np(dq)
+        out["dk"] = [to_np(t) for t in dks]
+        out["dv"] = [to_np(t) for t in dvs]
+    torch.cuda.synchronize()
+    host = {"q": qv, "k": kv, "v": vv, "do": gv,
+            "qp": perm_np[rank * w.shard:(rank + 1) * w.shard],
+            "kps": [perm_np[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)],
+            "order": [(rank - t) % w.n_chunks for t in range(w.n_chunks)]}
+    return out, host
+
+
+@pytest.mark.parametrize("w", [RANK_FWD, GQA, MODALITY], ids=lambda w: w.name)
+def test_forward_full_size_sampled_rows(mm, w):
+    out, host = _run(mm, w)
+    edges = [w.granularity * k - 1 for k in range(1, 6)] + [w.granularity * k for k in range(1, 6)]
+    rows = _sample_rows(w.shard, extra_edges=edges if w.granularity else ())
+    o_ref, l_ref = oracle.ring_forward(host["q"], list(host["k"]), list(host["v"]), host["qp"],
+                                       host["kps"], order=host["order"], rows=rows)
+    assert_close_abs(out["o"][rows], o_ref, what=f"{w.name} O")
+    assert_close_abs(out["lse"][:, rows], l_ref, what=f"{w.name} LSE")
+    # every row of a shard sees at least its own diagonal key
+    assert np.isfinite(out["lse"]).all()
+
+
+def test_training_step_full_size(mm):
+    w = TRAIN
+    out, host = _run(mm, w, backward=True)
+    q, k, v, do = host["q"], host["k"], host["v"], host["do"]
+    qp, kps, order = host["qp"], host["kps"], host["order"]
+
+    # dQ on sampled rows (all heads): exact per-row oracle
+    rows = _sample_rows(w.shard, seed=1)
+    o_rows, l_rows = oracle.ring_forward(q, list(k), list(v), qp, kps, order=order, rows=rows)
+    assert_close_abs(out["o"][rows], o_rows, what="O rows")
+    delta_rows = oracle.bwd_delta(o_rows, do[rows])
+    dq_ref = np.zeros((len(rows), w.hq, w.d))
+    mq_ref = np.zeros((len(rows), w.hq, w.d))
+    for c in order:
+        dq_c, _, _ = oracle.attention_backward(q[rows], k[c], v[c], do[rows], l_rows, delta_rows,
+                                               qp[rows], kps[c])
+        mq_c, _, _ = oracle.attention_backward_magnitudes(q[rows], k[c], v[c], do[rows], o_rows,
+                                                          l_rows, qp[rows], kps[c])
+        dq_ref += dq_c
+        mq_ref += mq_c
+    assert_close_rms(out["dq"][rows], dq_ref, bound=mq_ref, what="dQ rows")
+
+    # two whole heads: every dK, dV of every chunk, within the rounding bound
+    for h in (5, 27):
+        q1, do1 = q[:, h:h + 1], do[:, h:h + 1]
+        k1 = [k[c][:, h:h + 1] for c in range(w.n_chunks)]
+        v1 = [v[c][:, h:h + 1] for c in range(w.n_chunks)]
+        o1, l1 = oracle.ring_forward(q1, k1, v1, qp, kps, order=order)
+        d1 = oracle.bwd_delta(o1, do1)
+        dk_ref, dv_ref, mk_ref, mv_ref = [], [], [], []
+        for c in range(w.n_chunks):
+            _, dk_c, dv_c = oracle.attention_backward(q1, k1[c], v1[c], do1, l1, d1, qp, kps[c])
+            _, mk_c, mv_c = oracle.attention_backward_magnitudes(q1, k1[c], v1[c], do1, o1, l1,
+                                                                 qp, kps[c])
+            dk_ref.append(dk_c[:, 0])
+            dv_ref.append(dv_c[:, 0])
+            mk_ref.append(mk_c[:, 0])
+            mv_ref.append(mv_c[:, 0])
+        assert_close_rms(np.stack([x[:, h] for x in out["dk"]]), np.stack(dk_ref),
+                         bound=np.stack(mk_ref), what=f"dK head {h}")
+        assert_close_rms(np.stack([x[:, h] for x in out["dv"]]), np.stack(dv_ref),
+                         bound=np.stack(mv_ref), what=f"dV head {h}")
+
+    # coarse identities over all heads and all keys (structural errors in any
+    # head).  Rounding the weights to bf16 perturbs each row's weight sum by up
+    # to u, independently across rows, so both sums drift like a random walk:
+    # allow 4 u sqrt(sum of squares) of the summed terms.
+    u = 2.0 ** -9
+    dk_sum = sum(x.astype(np.float64).sum(axis=0) for x in out["dk"])  # [hkv, d]
+    dk_l2 = np.sqrt(sum((x.astype(np.float64) ** 2).sum(axis=0) for x in out["dk"]))
+    assert np.all(np.abs(dk_sum) <= 4 * u * dk_l2 + 1e-6), "sum of dK over keys is not 0"
+    dv_sum = sum(x.astype(np.float64).sum(axis=0) for x in out["dv"])
+    want_dv = do.sum(axis=0)  # every row sees its own diagonal key
+    walk = np.sqrt((do.astype(np.float64) ** 2).sum(axis=0))
+    assert np.all(np.abs(dv_sum - want_dv) <= 4 * u * walk + 1e-4), "sum of dV over keys"

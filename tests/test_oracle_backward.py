@@ -3,7 +3,8 @@
 import numpy as np
 import pytest
 
-from oracle import attention_backward, attention_forward, bwd_delta, ring_forward
+from oracle import (attention_backward, attention_backward_magnitudes, attention_forward,
+                    bwd_delta, ring_forward)
 
 
 def _loss(q, ks, vs, qp, kps, do):
@@ -100,3 +101,24 @@ def test_empty_rows_have_zero_gradient(rng):
     dq, dk, dv = attention_backward(q, k, v, do, lse, bwd_delta(o, do), qp, kp)
     assert np.all(dq[:3] == 0)
     np.testing.assert_allclose(dv.sum(axis=0), do[3], rtol=1e-12)
+
+
+def test_magnitudes_bound_the_gradients(rng):
+    # triangle inequality: every gradient element is at most its sum of |terms|;
+    # with all-positive inputs and dO chosen so dS >= 0 the bound is tight for dV
+    n, hq, hkv, d = 40, 4, 2, 8
+    q = rng.standard_normal((n, hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    v = rng.standard_normal((n, hkv, d))
+    do = rng.standard_normal((n, hq, d))
+    pos = np.arange(n)
+    o, lse = attention_forward(q, k, v, pos, pos)
+    dq, dk, dv = attention_backward(q, k, v, do, lse, bwd_delta(o, do), pos, pos)
+    mq, mk, mv = attention_backward_magnitudes(q, k, v, do, o, lse, pos, pos)
+    assert np.all(np.abs(dq) <= mq + 1e-12)
+    assert np.all(np.abs(dk) <= mk + 1e-12)
+    assert np.all(np.abs(dv) <= mv + 1e-12)
+    do_pos = np.abs(do)
+    _, _, dv2 = attention_backward(q, k, v, do_pos, lse, bwd_delta(o, do_pos), pos, pos)
+    _, _, mv2 = attention_backward_magnitudes(q, k, v, do_pos, o, lse, pos, pos)
+    np.testing.assert_allclose(dv2, mv2, rtol=1e-12, atol=1e-12)
