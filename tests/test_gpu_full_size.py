@@ -3,10 +3,10 @@ bench.py times (GPU shard balance -> fused ring forward -> backward).
 
 The oracle cannot redo whole 8K x 64K attentions in seconds, so outputs are
 compared on sampled query rows (all heads; rows at tile, half and block
-boundaries plus seeded random rows), on one whole head for the backward, and
-through identities that hold at any size:
-  sum over all keys of all chunks of dK = 0 (softmax shift invariance) and
-  sum over all keys of dV = sum of dO over rows that see any key.
+boundaries plus seeded random rows), on whole heads for dK/dV (elementwise,
+within the bf16 rounding bound), and through an identity that holds at any
+size: the sum of dV over all keys of all chunks equals the sum of dO over the
+rows that see any key (each row's weights sum to one).
 """
 
 import numpy as np
@@ -115,8 +115,8 @@ def test_training_step_full_size(mm):
         mq_ref += mq_c
     assert_close_rms(out["dq"][rows], dq_ref, bound=mq_ref, what="dQ rows")
 
-    # two whole heads: every dK, dV of every chunk, within the rounding bound
-    for h in (5, 27):
+    # three whole heads: every dK, dV of every chunk, within the rounding bound
+    for h in (0, 17, 31):
         q1, do1 = q[:, h:h + 1], do[:, h:h + 1]
         k1 = [k[c][:, h:h + 1] for c in range(w.n_chunks)]
         v1 = [v[c][:, h:h + 1] for c in range(w.n_chunks)]
@@ -136,15 +136,13 @@ def test_training_step_full_size(mm):
         assert_close_rms(np.stack([x[:, h] for x in out["dv"]]), np.stack(dv_ref),
                          bound=np.stack(mv_ref), what=f"dV head {h}")
 
-    # coarse identities over all heads and all keys (structural errors in any
-    # head).  Rounding the weights to bf16 perturbs each row's weight sum by up
-    # to u, independently across rows, so both sums drift like a random walk:
-    # allow 4 u sqrt(sum of squares) of the summed terms.
+    # every head: the weights of each row sum to one, so summing dV over all
+    # keys of all chunks gives the sum of dO over the rows (each row sees its
+    # own diagonal key).  The bf16 weights of a row sum to one within u, so the
+    # two sums differ by at most u * sum |dO| (a dropped chunk or row block
+    # would exceed it).
     u = 2.0 ** -9
-    dk_sum = sum(x.astype(np.float64).sum(axis=0) for x in out["dk"])  # [hkv, d]
-    dk_l2 = np.sqrt(sum((x.astype(np.float64) ** 2).sum(axis=0) for x in out["dk"]))
-    assert np.all(np.abs(dk_sum) <= 4 * u * dk_l2 + 1e-6), "sum of dK over keys is not 0"
     dv_sum = sum(x.astype(np.float64).sum(axis=0) for x in out["dv"])
-    want_dv = do.sum(axis=0)  # every row sees its own diagonal key
-    walk = np.sqrt((do.astype(np.float64) ** 2).sum(axis=0))
-    assert np.all(np.abs(dv_sum - want_dv) <= 4 * u * walk + 1e-4), "sum of dV over keys"
+    want_dv = do.sum(axis=0)
+    bound = u * np.abs(do.astype(np.float64)).sum(axis=0) + 1e-3
+    assert np.all(np.abs(dv_sum - want_dv) <= bound), "sum of dV over keys"
