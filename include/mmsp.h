@@ -157,9 +157,11 @@ int mmsp_attn_bwd_preprocess(const void* o, const void* dout, int32_t sq, int32_
  * (lse = final merged LSE over all chunks; rows with lse = -inf contribute
  * nothing); q_pos/k_pos as in mmsp_attn_fwd_chunk.
  * dq_acc fp32 [sq][hq][d]: this chunk's dQ is ADDED (zero it before the first
- *   chunk); additions use device atomics, so the summation order -- and the
- *   last bits of dq_acc -- may differ between runs.
+ *   chunk).  Each element is read, summed and written once per call by one
+ *   thread (no atomics), so results are deterministic run to run.
  * dk, dv fp32 [sk][hkv][d]: overwritten, or added to with MMSP_ACCUMULATE.
+ * Two kernels are enqueued on the stream (dK/dV, then dQ); the call must not
+ *   overlap another call that writes the same dq_acc, dk or dv.
  */
 int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void* dout,
                         const float* lse, const float* delta, const int32_t* q_pos,
