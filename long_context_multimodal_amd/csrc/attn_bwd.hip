@@ -238,6 +238,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
         dsk[2 * g] = pack_bf16x2(dsv[0], dsv[1]);
         dsk[2 * g + 1] = pack_bf16x2(dsv[2], dsv[3]);
       }
+      __builtin_amdgcn_sched_barrier(0);
       // dV^T += dO^T P and dK^T += Q^T dS  (row = head dim, col = key, k = query)
 #pragma unroll
       for (int ks = 0; ks < C::BQ / 16; ++ks) {
@@ -254,6 +255,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
                                    dkacc[mb]);
         }
       }
+      // keep 8 transposing reads in flight ahead of the MFMA that consumes them
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     if (it + 1 < total) {
       publish_tile(BUF ^ 1);

@@ -17,9 +17,13 @@
 // here are free of bank conflicts: 16 lanes reading one chunk of 16
 // consecutive rows (ds_read_b128), and the transposing read of 4 rows x 4
 // chunks per 32 lanes (ds_read_b64_tr_b16).  Tiles are filled by direct
-// global->LDS loads (global_load_lds_dwordx4): lane l of a wave writes LDS
+// buffer->LDS loads (buffer_load_dwordx4 ... lds): lane l of a wave writes LDS
 // bytes [16 l, 16 l + 16) of the wave's 1 KiB window, so the swizzle is
-// applied by choosing which global chunk each lane fetches.
+// applied by choosing which global chunk each lane fetches.  The buffer
+// (MUBUF) form is used rather than global_load_lds: a FLAT-encoded load in
+// flight makes the compiler treat LDS reads as completing out of order, so it
+// would wait for all of them (lgkmcnt(0)) before every use instead of only
+// for the one being consumed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -101,10 +105,37 @@ __device__ __forceinline__ int tile_off(int row, int c) {
   return row * (D * 2) + ((c ^ swz<D>(row)) << 4);
 }
 
-// Direct global->LDS fill of a ROWS x D bf16 tile by THREADS threads.
+// Buffer resource over [base, base + nbytes) (raw, stride 0; gfx9 dword 3 =
+// 32-bit data format).  The base is taken from lane 0: callers pass
+// wave-uniform addresses, and reading it through readfirstlane keeps the
+// descriptor in scalar registers without a waterfall loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)u, (short)0, (int)nbytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t clamp_bytes(size_t n) {
+  return n > 0xffffffffull ? 0xffffffffu : (uint32_t)n;
+}
+
+// Direct LDS fill from a buffer: lane l writes SIZE bytes at dst + SIZE * l
+// (dst wave-uniform), read from byte voff of the buffer; lanes whose voff is
+// out of the buffer's range write zeros.
+template <int SIZE>
+__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                              lds_char* dst) {
+  static_assert(SIZE == 16 || SIZE == 4, "direct LDS load of 4 or 16 bytes per lane");
+  auto* d = (__attribute__((address_space(3))) void*)dst;
+  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 4, voff, 0, 0, 0);
+}
+
+// Direct buffer->LDS fill of a ROWS x D bf16 tile by THREADS threads.
 // Tile row r lives at global element offset r * row_stride from `base`.
-// Per-lane byte offsets (loop invariant, from tile_src_offsets) are added to a
-// wave-uniform base, so the loads use the scalar-base + 32-bit-offset form.
+// Per-lane byte offsets (loop invariant) index a buffer descriptor built on
+// the wave-uniform tile base.
 template <int D, int ROWS, int THREADS>
 struct TileLoader {
   static constexpr int CPR = D / 8;
@@ -113,9 +144,11 @@ struct TileLoader {
   uint32_t off[ROUNDS];   // byte offset of this lane's chunk, row 0 = tile row 0
   int row[ROUNDS];        // tile row of this lane's chunk in each round
   int wave_base;
+  size_t row_bytes;       // global bytes between consecutive tile rows
 
   __device__ __forceinline__ void init(int tid, size_t row_stride) {
     wave_base = uniform((tid >> 6) << 6);
+    row_bytes = row_stride * 2;
     const int lane = tid & 63;
 #pragma unroll
     for (int c = 0; c < ROUNDS; ++c) {
@@ -128,23 +161,19 @@ struct TileLoader {
   }
   // all rows of the tile exist: base points at tile row 0
   __device__ __forceinline__ void load(lds_char* tile, const uint16_t* base) const {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, clamp_bytes((size_t)ROWS * row_bytes));
 #pragma unroll
-    for (int c = 0; c < ROUNDS; ++c)
-      __builtin_amdgcn_global_load_lds((const char*)base + off[c],
-                                       (__attribute__((address_space(3))) void*)(
-                                           tile + (c * THREADS + wave_base) * 16),
-                                       16, 0, 0);
+    for (int c = 0; c < ROUNDS; ++c) buffer_to_lds<16>(rs, off[c], tile + (c * THREADS + wave_base) * 16);
   }
   // tail tile: rows at or past `rows_left` re-read the last existing row
   __device__ __forceinline__ void load_clamped(lds_char* tile, const uint16_t* base,
                                                size_t row_stride, int rows_left) const {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, clamp_bytes((size_t)rows_left * row_bytes));
 #pragma unroll
     for (int c = 0; c < ROUNDS; ++c) {
       const int back = row[c] - min(row[c], rows_left - 1);
-      const char* src = (const char*)base + off[c] - (size_t)back * row_stride * 2;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(
-                                                tile + (c * THREADS + wave_base) * 16),
-                                       16, 0, 0);
+      buffer_to_lds<16>(rs, off[c] - (uint32_t)((size_t)back * row_stride * 2),
+                        tile + (c * THREADS + wave_base) * 16);
     }
   }
 };
@@ -173,8 +202,8 @@ __device__ __forceinline__ void wait_vmem_le() {
 __device__ __forceinline__ void pos_load_direct(lds_char* slot, const int32_t* src, int j0,
                                                 int valid) {
   const int l = threadIdx.x & 63;
-  __builtin_amdgcn_global_load_lds(src + j0 + min(l, valid - 1),
-                                   (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + j0, (uint32_t)valid * 4u);
+  buffer_to_lds<4>(rs, (uint32_t)min(l, valid - 1) * 4u, slot);
 }
 
 // A operand rows = tile rows (k = head dim): lane reads chunk c of row r.
