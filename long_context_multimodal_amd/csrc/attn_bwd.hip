@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -140,17 +140,20 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   const size_t q_row_stride = (size_t)p.hq * D;
   TileLoader<D, C::BQ, C::THREADS> ld;
   ld.init(tid, q_row_stride);
-  float lreg = INFINITY, dreg = 0.f;
-  int preg = INT_MIN;
+  uint32_t stat = 0;
+  bool row_live = false;
 
-  auto tile_of = [&](int it, int& h, int& q0) {
-    const int gi = it / per_head;
-    h = kvh * p.group + gi;
-    q0 = (qt0 + it % per_head) * C::BQ;
-  };
-  auto issue_tile = [&](int it, auto buf) {
-    int h, q0;
-    tile_of(it, h, q0);
+  // Tiles in order: query heads kvh*G .. kvh*G+G-1, each over query tiles
+  // qt0 .. n_qt-1.  Tiles are fetched in sequence, so the next one is tracked
+  // by counters rather than recomputed with divisions.
+  int nx_h = kvh * p.group, nx_q0 = qt0 * C::BQ;
+  auto issue_next = [&](auto buf) {
+    const int h = nx_h, q0 = nx_q0;
+    nx_q0 += C::BQ;
+    if (nx_q0 >= n_qt * C::BQ) {
+      nx_q0 = qt0 * C::BQ;
+      ++nx_h;
+    }
     const size_t o = (size_t)q0 * q_row_stride + (size_t)h * D;
     if (q0 + C::BQ <= p.sq) {
       ld.load(qtile(buf), p.q + o);
@@ -159,29 +162,32 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
       ld.load_clamped(qtile(buf), p.q + o, q_row_stride, p.sq - q0);
       ld.load_clamped(otile(buf), p.dout + o, q_row_stride, p.sq - q0);
     }
-    if (tid < C::BQ) {
-      const int i = q0 + tid;
-      if (i < p.sq) {
-        const float l = p.lse[(size_t)h * p.sq + i];
-        lreg = (l == -INFINITY) ? INFINITY : l * kLog2e;
-        dreg = p.delta[(size_t)h * p.sq + i];
-        preg = p.causal ? p.q_pos[i] : (kPosInf - 1);
-      } else {
-        lreg = INFINITY;
-        dreg = 0.f;
-        preg = INT_MIN;
-      }
-    } else if (tid == C::BQ) {
-      preg = p.causal ? p.q_pos[min(q0 + C::BQ - 1, p.sq - 1)] : (kPosInf - 1);
+    // Per-row statistics, one array per wave (1: LSE, 2: delta, 3: positions,
+    // its lane BQ fetching the tile's last position), all into the one
+    // register `stat` from a wave-selected base.  Raw values only: they are
+    // converted when published, after the wait that ends the step, so no
+    // load here is waited for inside the step.
+    if (wave != 0 && lane <= C::BQ) {
+      const int i = min(q0 + min(lane, C::BQ - 1), p.sq - 1);
+      const uint32_t* src = wave == 1   ? (const uint32_t*)p.lse + (size_t)h * p.sq
+                            : wave == 2 ? (const uint32_t*)p.delta + (size_t)h * p.sq
+                            : p.causal  ? (const uint32_t*)p.q_pos
+                                        : (const uint32_t*)p.lse;  // any readable row
+      stat = src[i];
+      row_live = q0 + lane < p.sq;
     }
   };
   auto publish_tile = [&](int buf) {
-    if (tid < C::BQ) {
-      sL[buf][tid] = lreg;
-      sDl[buf][tid] = dreg;
-      sQp[buf][tid] = preg;
-    } else if (tid == C::BQ) {
-      sQlast[buf] = preg;
+    if (wave == 1 && lane < C::BQ) {
+      // empty rows (LSE = -inf) and rows past sq get P = exp2(s c - inf) = 0
+      const float l = __uint_as_float(stat);
+      sL[buf][lane] = (row_live && l != -INFINITY) ? l * kLog2e : INFINITY;
+    } else if (wave == 2 && lane < C::BQ) {
+      sDl[buf][lane] = row_live ? __uint_as_float(stat) : 0.f;
+    } else if (wave == 3 && lane <= C::BQ) {
+      const int pos = p.causal ? (int)stat : kPosInf - 1;
+      if (lane < C::BQ) sQp[buf][lane] = row_live ? pos : INT_MIN;
+      else sQlast[buf] = pos;
     }
   };
 
@@ -196,7 +202,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   auto step = [&](auto buf_tag, int it) {
     constexpr int BUF = decltype(buf_tag)::value;
     using Next = std::integral_constant<int, BUF ^ 1>;
-    if (it + 1 < total) issue_tile(it + 1, Next{});
+    if (it + 1 < total) issue_next(Next{});
     const lds_char* qt = qtile(buf_tag);
     const lds_char* dt = otile(buf_tag);
     const int qfirst = uniform(sQp[BUF][0]);
@@ -272,7 +278,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   };
 
   if (total > 0) {
-    issue_tile(0, B0{});
+    issue_next(B0{});
     publish_tile(0);
   }
   wait_vmem();
@@ -409,6 +415,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   TileLoader<D, C::BN, C::THREADS> ld;
   ld.init(tid, kv_row_stride);
   int kpreg = kPosInf;
+  bool key_live = false;
   auto issue_tile = [&](int t, auto buf) {
     const int j0 = t * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
@@ -419,9 +426,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
       ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, p.sk - j0);
       ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, p.sk - j0);
     }
-    if (tid < C::BN) {
-      const int j = j0 + tid;
-      kpreg = (j < p.sk) ? (p.causal ? p.k_pos[j] : 0) : kPosInf;
+    if (tid < C::BN) {  // raw position; keys past sk are hidden when published
+      kpreg = p.causal ? p.k_pos[min(j0 + tid, p.sk - 1)] : 0;
+      key_live = j0 + tid < p.sk;
     }
   };
 
@@ -480,7 +487,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
       }
     }
     if (t + 1 < nt) {
-      if (tid < C::BN) kpos_of(Next{})[tid] = kpreg;
+      if (tid < C::BN) kpos_of(Next{})[tid] = key_live ? kpreg : kPosInf;
       wait_vmem();
     }
     __syncthreads();
@@ -488,7 +495,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
 
   if (nt > 0) {
     issue_tile(0, B0{});
-    if (tid < C::BN) sKp0[tid] = kpreg;
+    if (tid < C::BN) sKp0[tid] = key_live ? kpreg : kPosInf;
     wait_vmem();
   }
   __syncthreads();
