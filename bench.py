@@ -37,9 +37,13 @@ METRIC = "causal attn TFLOP/s per rank shard (fwd, fwd+bwd); % of MI355X bf16 MF
 # MI355X dense bf16 MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz (published 2.5 PFLOP/s)
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
+# sources whose text decides each kernel's memory traffic (the kernel and the
+# shared tile loaders); a stored counter reading is used only while they match
 KERNEL_SRC = {
-    "attn_bwd_chunk": "long_context_multimodal_amd/csrc/attn_bwd.hip",
-    "attn_fwd_chunk": "long_context_multimodal_amd/csrc/attn_fwd.hip",
+    "attn_bwd_chunk": ("long_context_multimodal_amd/csrc/attn_bwd.hip",
+                       "long_context_multimodal_amd/csrc/common.h"),
+    "attn_fwd_chunk": ("long_context_multimodal_amd/csrc/attn_fwd.hip",
+                       "long_context_multimodal_amd/csrc/common.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -120,8 +124,11 @@ def visible_pairs_per_chunk(w, perm_np, rank):
     return out
 
 
-def source_sha(path):
-    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+def source_sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(os.path.join(ROOT, path), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel):
