@@ -77,7 +77,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int kvh = logical / p.n_ktiles;
-  const int kt = logical % p.n_ktiles;  // early keys (more visible queries) first
+  // early keys see more queries: their end of the range is dispatched first
+  const int kt = p.n_ktiles - 1 - heavy_first_tile(logical % p.n_ktiles, p.n_ktiles, gridDim.x);
   const int j0 = kt * C::BK;
   const int key = j0 + wave * 32 + l32;
   const bool key_ok = key < p.sk;
@@ -348,7 +349,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int h = logical / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - (logical % p.n_qtiles);
+  const int qt = heavy_first_tile(logical % p.n_qtiles, p.n_qtiles, gridDim.x);
   const int kvh = h / p.group;
   const int q0 = qt * C::BM;
   const int row = q0 + wave * 32 + l32;

@@ -12,8 +12,9 @@
 // waves per SIMD):
 //  * each wave owns 32 query rows; Q stays in registers; the 8 waves share
 //    every K/V tile, so each tile crosses HBM/L2 -> LDS once per 256 rows;
-//  * K/V tiles of 64 keys go straight from HBM to a 3-stage, XOR-swizzled
-//    LDS ring with 16-byte direct loads (no staging registers); each stage
+//  * K/V tiles of 64 keys go straight from HBM to a 4-stage, XOR-swizzled
+//    LDS ring with 16-byte direct loads (no staging registers), three tiles
+//    in flight ahead of the one being used; each stage
 //    is its own LDS object so loads into one never stall reads of another;
 //    the key positions of a tile are loaded directly into a per-wave slot;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a lane holds 16 scores of ONE
@@ -29,7 +30,9 @@
 //    the key range of the workgroup, each wave skips tiles it cannot see and
 //    masks only the tiles that straddle its rows' positions (or the tail);
 //  * GQA: query head h reads KV head h / G; the workgroup order keeps the
-//    query heads of one KV head on one XCD (shared L2).
+//    query heads of one KV head on one XCD (shared L2), and within a head
+//    alternates heavy and light query tiles so every XCD's share is
+//    balanced (the two zigzag blocks of a shard see different key counts).
 #include <type_traits>
 
 #include "common.h"
@@ -45,7 +48,7 @@ struct FwdCfg {
   static constexpr int QB = 1;                // 32-row query blocks per wave
   static constexpr int BM = WAVES * 32 * QB;  // query rows per workgroup
   static constexpr int BN = 64;               // keys per tile
-  static constexpr int NS = 3;                // pipeline stages
+  static constexpr int NS = 4;                // pipeline stages (K/V tiles in flight + 1)
   static constexpr int KS = D / 16;           // K-steps of S^T = K Q^T
   static constexpr int MB = D / 32;           // 32-row blocks of O^T
   static constexpr int NKB = BN / 32;         // 32-key blocks per tile
@@ -58,31 +61,38 @@ template <int D, bool ACC>
 __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   // one LDS object per pipeline stage
-  __shared__ __attribute__((aligned(16))) char sK0[C::TILE], sK1[C::TILE], sK2[C::TILE];
-  __shared__ __attribute__((aligned(16))) char sV0[C::TILE], sV1[C::TILE], sV2[C::TILE];
+  static_assert(C::NS == 4, "stage objects below are written out for four stages");
+  __shared__ __attribute__((aligned(16))) char sK0[C::TILE], sK1[C::TILE], sK2[C::TILE],
+      sK3[C::TILE];
+  __shared__ __attribute__((aligned(16))) char sV0[C::TILE], sV1[C::TILE], sV2[C::TILE],
+      sV3[C::TILE];
   __shared__ __attribute__((aligned(16))) int sP0[C::WAVES * C::BN], sP1[C::WAVES * C::BN],
-      sP2[C::WAVES * C::BN];
+      sP2[C::WAVES * C::BN], sP3[C::WAVES * C::BN];
   auto ktile = [&](auto b) -> lds_char* {
     constexpr int S = decltype(b)::value;
     if constexpr (S == 0) return (lds_char*)sK0;
     else if constexpr (S == 1) return (lds_char*)sK1;
-    else return (lds_char*)sK2;
+    else if constexpr (S == 2) return (lds_char*)sK2;
+    else return (lds_char*)sK3;
   };
   auto vtile = [&](auto b) -> lds_char* {
     constexpr int S = decltype(b)::value;
     if constexpr (S == 0) return (lds_char*)sV0;
     else if constexpr (S == 1) return (lds_char*)sV1;
-    else return (lds_char*)sV2;
+    else if constexpr (S == 2) return (lds_char*)sV2;
+    else return (lds_char*)sV3;
   };
   auto ptile = [&](auto b) -> int* {
     constexpr int S = decltype(b)::value;
     if constexpr (S == 0) return sP0;
     else if constexpr (S == 1) return sP1;
-    else return sP2;
+    else if constexpr (S == 2) return sP2;
+    else return sP3;
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,7 +102,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int h = logical / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - (logical % p.n_qtiles);  // late (heavier) tiles first
+  const int qt = heavy_first_tile(logical % p.n_qtiles, p.n_qtiles, gridDim.x);
   const int kvh = h / p.group;
   const int q0 = qt * C::BM;
   const int wr0 = q0 + wave * 32 * C::QB;  // first row of this wave
@@ -187,10 +197,13 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   // one K/V tile; STAGE is compile-time so every LDS object and offset is fixed
   auto step = [&](auto stage, int t) {
     constexpr int ST = decltype(stage)::value;
-    using Ahead = std::integral_constant<int, (ST + 2) % 3>;
-    if (t + 1 < nt) wait_vmem_le<C::VMEM>(); else wait_vmem_le<0>();
+    using Ahead = std::integral_constant<int, (ST + C::NS - 1) % C::NS>;
+    // tile t complete; the tiles after it that were issued stay in flight
+    if (t + 2 < nt) wait_vmem_le<2 * C::VMEM>();
+    else if (t + 1 < nt) wait_vmem_le<C::VMEM>();
+    else wait_vmem_le<0>();
     barrier_only();  // tile t visible to all waves; stage of tile t-1 free
-    if (t + 2 < nt) issue_tile(t + 2, Ahead{});
+    if (t + 3 < nt) issue_tile(t + 3, Ahead{});
     const lds_char* kt = ktile(stage);
     const lds_char* vt = vtile(stage);
     const int* kp = ptile(stage) + wave * C::BN;
@@ -277,10 +290,12 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
 
   if (nt > 0) issue_tile(0, S0{});
   if (nt > 1) issue_tile(1, S1{});
-  for (int t = 0; t < nt; t += 3) {
+  if (nt > 2) issue_tile(2, S2{});
+  for (int t = 0; t < nt; t += 4) {
     step(S0{}, t);
     if (t + 1 < nt) step(S1{}, t + 1);
     if (t + 2 < nt) step(S2{}, t + 2);
+    if (t + 3 < nt) step(S3{}, t + 3);
   }
 
   // ---- epilogue: normalise, then write or merge ----

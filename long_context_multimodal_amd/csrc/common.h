@@ -92,6 +92,26 @@ __device__ __forceinline__ int xcd_logical_block(int b, int n) {
   return (b & 7) * (n >> 3) + (b >> 3);
 }
 
+// Order of the n tiles of one head, given the dispatch index i within the
+// head, so that the heavy end (tile n-1: late queries, or early keys once the
+// caller reverses it) is dispatched first.
+//
+// When one head's tiles fill less than an XCD's share of the grid (each XCD
+// runs a contiguous range of logical tiles), whole heads share an XCD and the
+// plain heavy-first order is used.  When a head spans several XCDs, a plain
+// order would hand one XCD only heavy tiles and the next only light ones (the
+// two blocks of a zigzag shard: one may see none of a chunk), so the order
+// alternates between the two ends in blocks of 8 tiles: blocks n/8-1, 0,
+// n/8-2, 1, ... each in natural order.  Runs of 8 keep consecutive
+// workgroups -- which the dispatcher deals to different shader engines of an
+// XCD -- of one kind, so no engine collects only the heavy tiles.
+__device__ __forceinline__ int heavy_first_tile(int i, int n, int grid) {
+  if ((n << 3) <= grid || (n & 7) != 0) return n - 1 - i;
+  const int nb = n >> 3, bi = i >> 3;
+  const int blk = (bi & 1) ? (bi >> 1) : nb - 1 - (bi >> 1);
+  return (blk << 3) | (i & 7);
+}
+
 // ---- swizzled LDS tiles -----------------------------------------------------
 template <int D>
 __device__ __forceinline__ constexpr int swz(int r) {
