@@ -46,6 +46,8 @@ KERNEL_SRC = {
                        "long_context_multimodal_amd/csrc/common.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+# oracle work timed for the CPU baseline, at most (about 30 s at 0.1 TFLOP/s)
+CPU_BASELINE_FLOP_BUDGET = 3.0e12
 
 
 def log(msg):
@@ -168,19 +170,32 @@ def cpu_baseline(w, rank, perm_np):
     qp = rank_positions(perm_np, w, rank)
     kps = [perm_np[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
     order = [(rank - t) % w.n_chunks for t in range(w.n_chunks)]
+    per_pair = (4 + (10 if w.backward else 0)) * w.d * nh
+    # all rows when that is at most ~30 s of oracle work, else a seeded random
+    # subset of query rows (each row's work is counted exactly)
+    rows = None
+    flops_all = per_pair * sum(visible_pairs_per_chunk(w, perm_np, rank))
+    if flops_all > CPU_BASELINE_FLOP_BUDGET:
+        n_rows = max(64, int(w.shard * CPU_BASELINE_FLOP_BUDGET / flops_all))
+        rows = np.sort(np.random.default_rng(0).choice(w.shard, n_rows, replace=False))
+    qr = qp if rows is None else qp[rows]
     log(f"[bench] cpu_baseline inputs ready in {time.time() - t_gen:.1f}s")
     t0 = time.time()
-    o, lse = oracle.ring_forward(q1, k1, v1, qp, kps, order=order)
+    o, lse = oracle.ring_forward(q1, k1, v1, qp, kps, order=order, rows=rows)
     t_fwd = time.time() - t0
     t_bwd = 0.0
     if g1 is not None:
         t1 = time.time()
-        delta = oracle.bwd_delta(o, g1)
+        g1r = g1 if rows is None else g1[rows]
+        q1r = q1 if rows is None else q1[rows]
+        delta = oracle.bwd_delta(o, g1r)
         for c in order:
-            oracle.attention_backward(q1, k1[c], v1[c], g1, lse, delta, qp, kps[c])
+            oracle.attention_backward(q1r, k1[c], v1[c], g1r, lse, delta, qr, kps[c])
         t_bwd = time.time() - t1
-    pairs = sum(visible_pairs_per_chunk(w, perm_np, rank))
-    flops = (4 + (10 if w.backward else 0)) * w.d * pairs * nh
+    pairs = 0
+    for c in range(w.n_chunks):
+        pairs += int(np.searchsorted(np.sort(kps[c]), qr, side="right").sum())
+    flops = per_pair * pairs
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     elapsed = t_fwd + t_bwd
     return {
@@ -188,9 +203,12 @@ def cpu_baseline(w, rank, perm_np):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"query heads 0-{nh - 1} of {w.hq} ({nh}/{w.hq} of the step's FLOPs), all "
-                   f"{w.shard} query "
-                   f"rows, all {w.n_chunks} chunks, forward{' + backward' if w.backward else ''}; "
+        "sample": (f"query heads 0-{nh - 1} of {w.hq}, "
+                   + (f"all {w.shard} query rows" if rows is None else
+                      f"{len(rows)} seeded random query rows of {w.shard}")
+                   + f" ({flops / (per_pair / nh * w.hq) / sum(visible_pairs_per_chunk(w, perm_np, rank)):.4f}"
+                   f" of the step's FLOPs), all {w.n_chunks} chunks, "
+                   f"forward{' + backward' if w.backward else ''}; "
                    f"fwd {t_fwd:.1f}s bwd {t_bwd:.1f}s; host affinity "
                    f"{len(os.sched_getaffinity(0))} cpus, BLAS threads {threads}"),
     }

@@ -141,4 +141,16 @@ TRAIN = Workload("zigzag_p8_shard8192_h32_d128_fwd_bwd", 65536, 8, 32, 32, 128, 
                  backward=True,
                  note="rank 0 of zigzag P=8, forward + backward over 8 KV chunks")
 
-WORKLOADS = {w.name: w for w in (TINY, RANK_FWD, GQA, MODALITY, TRAIN)}
+# The per-GPU share after the intra-node all-to-all of the hybrid scheme: a
+# 2,097,152-token context over a ring of 32 node groups (65,536 tokens each)
+# whose 8 GPUs split the 32 heads, 4 per GPU ("LongVILA Guide: 2M Context
+# Multi-Modal AI Model", "Multi-Modal Sequence Parallelism (MM-SP)
+# Mechanics", items 1-2): long rows, few heads, 32 ring steps.
+ULYSSES = Workload("ulysses_p32_shard65536_h4_d128", 2097152, 32, 4, 4, 128, "zigzag",
+                   note="rank 0 of a zigzag ring of 32 over 2,097,152 tokens, 4 heads per GPU: "
+                        "65,536-token Q shard vs 32 KV chunks of 65,536")
+ULYSSES_TRAIN = Workload("ulysses_p32_shard65536_h4_d128_fwd_bwd", 2097152, 32, 4, 4, 128,
+                         "zigzag", backward=True,
+                         note="as ulysses_p32_shard65536_h4_d128, forward + backward")
+
+WORKLOADS = {w.name: w for w in (TINY, RANK_FWD, GQA, MODALITY, TRAIN, ULYSSES, ULYSSES_TRAIN)}

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import oracle
-from long_context_multimodal_amd.workloads import GQA, MODALITY, RANK_FWD, TRAIN
+from long_context_multimodal_amd.workloads import (GQA, MODALITY, RANK_FWD, TRAIN, ULYSSES,
+                                                   ULYSSES_TRAIN)
 from tests.helpers import assert_close_abs, assert_close_rms, to_np
 
 pytestmark = pytest.mark.gpu
@@ -41,8 +42,12 @@ def _sample_rows(n, extra_edges=(), seed=0, n_random=16):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def _run(mm, w, backward=False, rank=0):
-    """Run the hot path on the GPU; return host copies and the oracle inputs."""
+def _run(mm, w, backward=False, rank=0, kv_grads="full"):
+    """Run the hot path on the GPU; return host copies and the oracle inputs.
+
+    ``kv_grads``: ``"full"`` copies every dK/dV chunk to the host, ``"dv_sum"``
+    only the float64 sum of dV over all keys of all chunks ([Hkv, d]).
+    """
     mmsp, ring = mm
     import torch
     qb, qv = w.q()
@@ -70,8 +75,12 @@ def _run(mm, w, backward=False, rank=0):
         gb, gv = w.do()
         dq, dks, dvs = ring.ring_backward(q, ks, vs, _dev_bf16(gb), o16, lse, qp, kps, rank=rank)
         out["dq"] = to_np(dq)
-        out["dk"] = [to_np(t) for t in dks]
-        out["dv"] = [to_np(t) for t in dvs]
+        if kv_grads == "full":
+            out["dk"] = [to_np(t) for t in dks]
+            out["dv"] = [to_np(t) for t in dvs]
+        else:
+            out["dv_sum"] = to_np(sum(t.double().sum(dim=0) for t in dvs))
+        del dks, dvs
     torch.cuda.synchronize()
     host = {"q": qv, "k": kv, "v": vv, "do": gv,
             "qp": perm_np[rank * w.shard:(rank + 1) * w.shard],
@@ -80,7 +89,7 @@ def _run(mm, w, backward=False, rank=0):
     return out, host
 
 
-@pytest.mark.parametrize("w", [RANK_FWD, GQA, MODALITY], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [RANK_FWD, GQA, MODALITY, ULYSSES], ids=lambda w: w.name)
 def test_forward_full_size_sampled_rows(mm, w):
     out, host = _run(mm, w)
     edges = [w.granularity * k - 1 for k in range(1, 6)] + [w.granularity * k for k in range(1, 6)]
@@ -146,3 +155,36 @@ def test_training_step_full_size(mm):
     want_dv = do.sum(axis=0)
     bound = u * np.abs(do.astype(np.float64)).sum(axis=0) + 1e-3
     assert np.all(np.abs(dv_sum - want_dv) <= bound), "sum of dV over keys"
+
+
+def _dq_rows_check(out, host, w, rows):
+    """dQ (all heads) on sampled rows against the exact per-row oracle."""
+    q, k, v, do = host["q"], host["k"], host["v"], host["do"]
+    qp, kps, order = host["qp"], host["kps"], host["order"]
+    o_rows, l_rows = oracle.ring_forward(q, list(k), list(v), qp, kps, order=order, rows=rows)
+    assert_close_abs(out["o"][rows], o_rows, what="O rows")
+    delta_rows = oracle.bwd_delta(o_rows, do[rows])
+    dq_ref = np.zeros((len(rows), w.hq, w.d))
+    mq_ref = np.zeros((len(rows), w.hq, w.d))
+    for c in order:
+        dq_c, _, _ = oracle.attention_backward(q[rows], k[c], v[c], do[rows], l_rows, delta_rows,
+                                               qp[rows], kps[c])
+        mq_c, _, _ = oracle.attention_backward_magnitudes(q[rows], k[c], v[c], do[rows], o_rows,
+                                                          l_rows, qp[rows], kps[c])
+        dq_ref += dq_c
+        mq_ref += mq_c
+    assert_close_rms(out["dq"][rows], dq_ref, bound=mq_ref, what="dQ rows")
+
+
+def test_ulysses_training_step_full_size(mm):
+    """The hybrid scheme's per-GPU share (65,536-token rows, 4 heads, 32 ring
+    steps over 2,097,152 tokens): O and dQ on sampled rows, and the dV-sum
+    identity over every key of all 32 chunks."""
+    w = ULYSSES_TRAIN
+    out, host = _run(mm, w, backward=True, kv_grads="dv_sum")
+    rows = _sample_rows(w.shard, seed=2, n_random=8)
+    _dq_rows_check(out, host, w, rows)
+    u = 2.0 ** -9
+    do = host["do"].astype(np.float64)
+    bound = u * np.abs(do).sum(axis=0) + 1e-3
+    assert np.all(np.abs(out["dv_sum"] - do.sum(axis=0)) <= bound), "sum of dV over keys"

@@ -9,7 +9,7 @@ import pytest
 
 from oracle import (causal_work_per_rank, inverse_perm, modality_perm,
                     visual_per_rank, zigzag_perm)
-from long_context_multimodal_amd.workloads import (FRAME_TOKENS, MODALITY, RANK_FWD,
+from long_context_multimodal_amd.workloads import (FRAME_TOKENS, MODALITY, RANK_FWD, ULYSSES,
                                                    frame_text_labels, tiny_labels)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_arithmetic.json")
@@ -132,6 +132,13 @@ def test_page_arithmetic_golden():
     # the per-rank workloads use the pages' per-rank shard and head count
     assert RANK_FWD.shard == gold["tokens_per_rank"]
     assert RANK_FWD.hq == gold["query_heads"]
+    # the hybrid scheme's per-GPU share: the ring runs over node groups and each
+    # GPU keeps all of its group's tokens for an eighth of the heads
+    assert ULYSSES.n_tokens == gold["max_seq_len"]
+    assert ULYSSES.n_ranks == gold["ring_size"] == ULYSSES.n_chunks
+    assert ULYSSES.shard == gold["max_seq_len"] // gold["ring_size"]
+    assert ULYSSES.hq == gold["heads_per_gpu_after_ulysses"]
+    assert ULYSSES.shard * ULYSSES.hq == gold["tokens_per_rank"] * gold["query_heads"]
 
 
 def test_frame_text_stream_shape():
