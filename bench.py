@@ -133,8 +133,9 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel):
-    """HBM bytes per launch from the committed counter summary, if current."""
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on this workload with the current kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     sha = source_sha(KERNEL_SRC[kernel])
@@ -142,9 +143,8 @@ def read_traffic(kernel):
         if not line.startswith(kernel + " "):
             continue
         kv = dict(tok.split("=", 1) for tok in line.split()[1:] if "=" in tok)
-        if kv.get("src_sha") != sha:
-            return None
-        return float(kv["hbm_bytes_per_launch"])
+        if kv.get("workload") == workload and kv.get("src_sha") == sha:
+            return float(kv["hbm_bytes_per_launch"])
     return None
 
 
@@ -223,6 +223,11 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--unfused", action="store_true", help="separate merge pass per chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring-copy", action="store_true",
+                    help="every KV chunk after the rank's own arrives by a device-to-device "
+                         "copy on a second stream while the previous chunk is computed (dK/dV "
+                         "copied out likewise); also times the resident ring and the copies "
+                         "alone and reports the overlap loss")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -266,8 +271,11 @@ def main():
         if w.backward else None
     contiguous_pos = torch.arange(n, dtype=torch.int32, device=device)
     timer = LaunchTimer()
+    rx = ring.ChunkReceiver(ks[0], vs[0]) if args.ring_copy else None
+    dk_sent = [torch.empty_like(t) for t in dks] if (rx is not None and w.backward) else None
+    dv_sent = [torch.empty_like(t) for t in dvs] if (rx is not None and w.backward) else None
 
-    def step():
+    def step(received=args.ring_copy):
         if mode is None:  # single rank holding every position, contiguous chunks
             perm = contiguous_pos
         else:
@@ -276,12 +284,32 @@ def main():
                                          with_inverse=False)
         qp = perm[rank * w.shard:(rank + 1) * w.shard]
         kps = [perm[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
+        if received:
+            ring.ring_forward_received(q, ks, vs, qp, kps, rx, rank=rank, fused=not args.unfused,
+                                       o=o, lse=lse, o_final=o16, timer=timer)
+            if w.backward:
+                ring.ring_backward_received(q, ks, vs, dout, o16, lse, qp, kps, rx, rank=rank,
+                                            dq=dq, dks=dks, dvs=dvs, dk_sent=dk_sent,
+                                            dv_sent=dv_sent, delta=delta, timer=timer)
+            return perm
         ring.ring_forward(q, ks, vs, qp, kps, rank=rank, fused=not args.unfused, o=o, lse=lse,
                           o_final=o16, timer=timer)
         if w.backward:
             ring.ring_backward(q, ks, vs, dout, o16, lse, qp, kps, rank=rank, dq=dq, dks=dks,
                                dvs=dvs, delta=delta, timer=timer)
         return perm
+
+    def copies_only():
+        """The copies one received step enqueues, without the compute."""
+        order = ring.ring_order(rank, w.n_chunks)
+        for _ in range(2 if w.backward else 1):
+            for t in range(1, w.n_chunks):
+                rx.receive(t, ks[order[t]], vs[order[t]])
+            if w.backward:
+                for c in order:
+                    rx.send(dk_sent[c], dks[c])
+                    rx.send(dv_sent[c], dvs[c])
+        rx.finish()
 
     log(f"[bench] warmup {args.warmup} steps")
     perm = None
@@ -317,7 +345,7 @@ def main():
         avg_ms = tot_ms / len(launches)
         achieved = tot_flop / (tot_ms * 1e-3) / 1e12
         name = "attn_bwd_chunk" if kind == "bwd" else "attn_fwd_chunk"
-        traffic = read_traffic(name)
+        traffic = read_traffic(name, w.name)
         return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -356,6 +384,8 @@ def main():
             "layout": w.layout, "rank": rank,
             "pass": "fwd+bwd" if w.backward else "fwd",
             "merge": "separate" if args.unfused else "fused into chunk epilogue",
+            "chunks": ("received by double-buffered copies" if args.ring_copy
+                       else "resident in HBM"),
         },
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_tflops, 2) if fwd_tflops else None,
@@ -367,6 +397,31 @@ def main():
         "roofline": bwd_rf if bwd_rf is not None else fwd_rf,
         "roofline_fwd": fwd_rf,
     }
+    if rx is not None:
+        def timed(fn):
+            torch.cuda.synchronize()
+            t_0 = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t_0) / args.steps * 1e3
+        rx.bytes_received = rx.bytes_sent = 0
+        copy_ms = timed(copies_only)
+        copy_bytes = (rx.bytes_received + rx.bytes_sent) / args.steps
+        resident_ms = timed(lambda: step(received=False))
+        result["ring_copy"] = {
+            "what": ("each KV chunk after the rank's own is copied device-to-device into one of "
+                     "two receive buffers on a second stream while the previous chunk is "
+                     "computed" + ("; each chunk's dK/dV are copied out the same way"
+                                   if w.backward else "")),
+            "ms_per_step_received": round(ms_per_step, 4),
+            "ms_per_step_resident": round(resident_ms, 4),
+            "overlap_loss_pct": round(100 * (ms_per_step - resident_ms) / resident_ms, 2),
+            "copy_only_ms_per_step": round(copy_ms, 4),
+            "copy_bytes_per_step": int(copy_bytes),
+            "copy_only_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+            "exposed_copy_pct": round(100 * max(0.0, ms_per_step - resident_ms) / copy_ms, 2),
+        }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w, rank, perm_np)

@@ -84,3 +84,150 @@ def ring_backward(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks,
         if timer is not None:
             timer.stop("bwd", c)
     return dq, dks, dvs
+
+
+class ChunkReceiver:
+    """Double-buffered arrival of ring chunks on one GPU.
+
+    The pages hide the ring exchange behind compute: while the attention of
+    the chunk held at step ``t`` runs, the next chunk is received from the
+    previous rank into a second buffer ("LongVILA Guide: 2M Context
+    Multi-Modal AI Model", section "Multi-Modal Sequence Parallelism (MM-SP)
+    Mechanics", item 3).  With one GPU the transfer is stood in for by a
+    device-to-device copy on a second stream (default priority) from the
+    chunk's resident storage into one of two receive buffers; the compute
+    stream waits for the copy of its chunk, and a copy into a buffer waits for
+    the compute that last read it.  In the backward the chunk's dK/dV are
+    likewise copied out (sent back to the owner) on the copy stream.
+    """
+
+    def __init__(self, like_k, like_v, device=None):
+        import torch
+        device = like_k.device if device is None else device
+        self.k = [torch.empty_like(like_k) for _ in range(2)]
+        self.v = [torch.empty_like(like_v) for _ in range(2)]
+        self.stream = torch.cuda.Stream(device=device)
+        self.copied = [torch.cuda.Event() for _ in range(2)]
+        self.consumed = [torch.cuda.Event() for _ in range(2)]
+        self.used = [False, False]
+        self.bytes_received = 0
+        self.bytes_sent = 0
+
+    def receive(self, step, k_src, v_src):
+        """Enqueue the copy of the chunk for ``step`` into buffer ``step % 2``."""
+        import torch
+        b = step % 2
+        with torch.cuda.stream(self.stream):
+            if self.used[b]:
+                self.stream.wait_event(self.consumed[b])
+            self.k[b].copy_(k_src, non_blocking=True)
+            self.v[b].copy_(v_src, non_blocking=True)
+            self.copied[b].record(self.stream)
+        self.bytes_received += k_src.numel() * k_src.element_size() * 2
+
+    def take(self, step):
+        """Make the current stream wait for the chunk of ``step``; return its buffers."""
+        import torch
+        b = step % 2
+        torch.cuda.current_stream().wait_event(self.copied[b])
+        return self.k[b], self.v[b]
+
+    def release(self, step):
+        """Mark the end, on the current stream, of the compute reading ``step``'s buffer."""
+        import torch
+        b = step % 2
+        self.consumed[b].record(torch.cuda.current_stream())
+        self.used[b] = True
+
+    def send(self, dst, src):
+        """Copy ``src`` (written on the current stream) to ``dst`` on the copy stream."""
+        import torch
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream())
+        with torch.cuda.stream(self.stream):
+            self.stream.wait_event(ev)
+            dst.copy_(src, non_blocking=True)
+        self.bytes_sent += src.numel() * src.element_size()
+
+    def finish(self):
+        """Make the current stream wait for every copy enqueued so far."""
+        import torch
+        torch.cuda.current_stream().wait_stream(self.stream)
+
+
+def ring_forward_received(q, k_chunks, v_chunks, q_pos, k_pos_chunks, receiver, rank=0,
+                          fused=True, scale=None, causal=True, o_final=None, o=None, lse=None,
+                          timer=None):
+    """``ring_forward`` in ring order, with every chunk after the rank's own
+    arriving through ``receiver`` (a :class:`ChunkReceiver`) while the previous
+    chunk is computed.  Same kernels and order, so the same results."""
+    import torch
+    n = len(k_chunks)
+    order = ring_order(rank, n)
+    o_part = lse_part = None
+    for step, c in enumerate(order):
+        if step == 0:
+            kc, vc = k_chunks[c], v_chunks[c]  # the rank's own chunk is local
+        else:
+            kc, vc = receiver.take(step)
+        if step + 1 < n:  # the next chunk arrives while this one is computed
+            receiver.receive(step + 1, k_chunks[order[step + 1]], v_chunks[order[step + 1]])
+        kp = k_pos_chunks[c] if causal else None
+        if timer is not None:
+            timer.start("fwd", c)
+        if step == 0:
+            o, lse = mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale, causal=causal, o=o,
+                                         lse=lse)
+        elif fused:
+            mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale, causal=causal, o=o, lse=lse,
+                                accumulate=True)
+        else:
+            o_part, lse_part = mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale,
+                                                   causal=causal, o=o_part, lse=lse_part)
+            mmsp.lse_merge(o, lse, o_part, lse_part)
+        if timer is not None:
+            timer.stop("fwd", c)
+        if step > 0:
+            receiver.release(step)
+    if o_final is None:
+        o_final = torch.empty(o.shape, dtype=torch.bfloat16, device=o.device)
+    mmsp.lse_merge(o, lse, None, None, o_final=o_final)
+    receiver.finish()
+    return o, lse, o_final
+
+
+def ring_backward_received(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks,
+                           receiver, rank=0, scale=None, causal=True, dq=None, dks=None,
+                           dvs=None, dk_sent=None, dv_sent=None, delta=None, timer=None):
+    """``ring_backward`` with chunks arriving through ``receiver`` and each
+    chunk's dK/dV sent (copied to ``dk_sent[c]``/``dv_sent[c]``) on the copy
+    stream as soon as they are computed."""
+    import torch
+    n = len(k_chunks)
+    order = ring_order(rank, n)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    delta = mmsp.attn_bwd_preprocess(o_bf16, dout, delta, dq_zero=dq)
+    dks = [None] * n if dks is None else dks
+    dvs = [None] * n if dvs is None else dvs
+    for step, c in enumerate(order):
+        if step == 0:
+            kc, vc = k_chunks[c], v_chunks[c]
+        else:
+            kc, vc = receiver.take(step)
+        if step + 1 < n:
+            receiver.receive(step + 1, k_chunks[order[step + 1]], v_chunks[order[step + 1]])
+        kp = k_pos_chunks[c] if causal else None
+        if timer is not None:
+            timer.start("bwd", c)
+        dks[c], dvs[c] = mmsp.attn_bwd_chunk(q, kc, vc, dout, lse, delta, q_pos, kp, dq,
+                                             dk=dks[c], dv=dvs[c], scale=scale, causal=causal)
+        if timer is not None:
+            timer.stop("bwd", c)
+        if step > 0:
+            receiver.release(step)
+        if dk_sent is not None:
+            receiver.send(dk_sent[c], dks[c])
+            receiver.send(dv_sent[c], dvs[c])
+    receiver.finish()
+    return dq, dks, dvs

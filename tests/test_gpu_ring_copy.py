@@ -1,0 +1,69 @@
+"""Ring with double-buffered chunk arrival (a second stream copies the next
+KV chunk while the current one is computed; dK/dV are copied out as they are
+produced): it runs the same kernels in the same order as the resident ring,
+so every output must be bit-identical, on repeated calls too."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.helpers import to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from long_context_multimodal_amd import mmsp, ring
+    mmsp.lib()
+    return mmsp, ring
+
+
+def _inputs(n_tokens, n_ranks, hq, hkv, d, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    perm = oracle.zigzag_perm(n_tokens, n_ranks)
+    shard = n_tokens // n_ranks
+
+    def t(shape):
+        return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).cuda().to(
+            torch.bfloat16)
+    q = t((shard, hq, d))
+    ks = [t((shard, hkv, d)) for _ in range(n_ranks)]
+    vs = [t((shard, hkv, d)) for _ in range(n_ranks)]
+    do = t((shard, hq, d))
+    pos = torch.from_numpy(perm.astype(np.int32)).cuda()
+    kps = [pos[c * shard:(c + 1) * shard] for c in range(n_ranks)]
+    return q, ks, vs, do, kps
+
+
+@pytest.mark.parametrize("rank", [0, 2])
+@pytest.mark.parametrize("fused", [True, False])
+def test_received_ring_matches_resident(mm, rank, fused):
+    import torch
+    mmsp, ring = mm
+    q, ks, vs, do, kps = _inputs(4096, 4, 8, 2, 128, seed=11 + rank)
+    qp = kps[rank]
+    o_a, l_a, o16_a = ring.ring_forward(q, ks, vs, qp, kps, rank=rank, fused=fused)
+    dq_a, dk_a, dv_a = ring.ring_backward(q, ks, vs, do, o16_a, l_a, qp, kps, rank=rank)
+    rx = ring.ChunkReceiver(ks[0], vs[0])
+    dk_sent = [torch.zeros(k.shape, dtype=torch.float32, device=k.device) for k in ks]
+    dv_sent = [torch.zeros(k.shape, dtype=torch.float32, device=k.device) for k in ks]
+    for _ in range(2):  # the receiver's buffers and events are reused
+        o_b, l_b, o16_b = ring.ring_forward_received(q, ks, vs, qp, kps, rx, rank=rank,
+                                                     fused=fused)
+        dq_b, dk_b, dv_b = ring.ring_backward_received(q, ks, vs, do, o16_b, l_b, qp, kps, rx,
+                                                       rank=rank, dk_sent=dk_sent,
+                                                       dv_sent=dv_sent)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b) and torch.equal(o16_a, o16_b)
+        assert torch.equal(dq_a, dq_b)
+        for c in range(len(ks)):
+            assert torch.equal(dk_a[c], dk_b[c]) and torch.equal(dv_a[c], dv_b[c])
+            assert torch.equal(dk_sent[c], dk_b[c]) and torch.equal(dv_sent[c], dv_b[c])
+    # every chunk but the rank's own arrived through the copy stream, twice per pass
+    per_chunk = ks[0].numel() * ks[0].element_size() * 2
+    assert rx.bytes_received == 2 * 2 * (len(ks) - 1) * per_chunk
+    assert np.isfinite(to_np(l_b)).all()
