@@ -41,6 +41,7 @@ from .merge import lse_merge, ring_forward  # noqa: F401
 from .backward import attention_backward, attention_backward_magnitudes, bwd_delta  # noqa: F401
 from .balance import (  # noqa: F401
     zigzag_perm,
+    zigzag_packed_perm,
     modality_perm,
     inverse_perm,
     causal_work_per_rank,

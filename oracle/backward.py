@@ -36,13 +36,13 @@ def bwd_delta(o, do):
     return np.einsum("ihc,ihc->hi", do, o)
 
 
-def attention_backward(q, k, v, do, lse, delta, q_pos, k_pos, scale=None):
+def attention_backward(q, k, v, do, lse, delta, q_pos, k_pos, scale=None, q_start=None):
     """Return ``(dq, dk, dv)`` of one chunk.
 
     ``q, do``: ``[Sq, Hq, d]``; ``k, v``: ``[Sk, Hkv, d]``; ``lse, delta``:
     ``[Hq, Sq]`` (final LSE over all chunks, and ``D`` from :func:`bwd_delta`).
     ``dq`` is this chunk's contribution ``[Sq, Hq, d]``; ``dk, dv`` are
-    ``[Sk, Hkv, d]``.
+    ``[Sk, Hkv, d]``.  ``q_start`` as in :func:`oracle.attention.attention_forward`.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -54,6 +54,8 @@ def attention_backward(q, k, v, do, lse, delta, q_pos, k_pos, scale=None):
     k_pos = np.asarray(k_pos, dtype=np.int64)
     sq, hq, d = q.shape
     sk, hkv, _ = k.shape
+    q_start = (np.full(sq, np.iinfo(np.int64).min, dtype=np.int64) if q_start is None
+               else np.asarray(q_start, dtype=np.int64))
     group = hq // hkv
     if scale is None:
         scale = 1.0 / np.sqrt(d)
@@ -67,10 +69,12 @@ def attention_backward(q, k, v, do, lse, delta, q_pos, k_pos, scale=None):
         for b0 in range(0, sq, _ROWS):
             r = slice(b0, min(b0 + _ROWS, sq))
             qp = q_pos[r]
-            cols = np.nonzero(k_pos <= qp.max())[0]
+            qs = q_start[r]
+            cols = np.nonzero((k_pos <= qp.max()) & (k_pos >= qs.min()))[0]
             if cols.size == 0:
                 continue
-            vis = k_pos[cols][None, :] <= qp[:, None]
+            kc = k_pos[cols][None, :]
+            vis = (kc <= qp[:, None]) & (kc >= qs[:, None])
             l_r = lse[h, r]
             live = np.isfinite(l_r)
             s = (q[r, h, :] @ kh[cols].T) * scale
@@ -84,7 +88,7 @@ def attention_backward(q, k, v, do, lse, delta, q_pos, k_pos, scale=None):
     return dq, dk, dv
 
 
-def attention_backward_magnitudes(q, k, v, do, o, lse, q_pos, k_pos, scale=None):
+def attention_backward_magnitudes(q, k, v, do, o, lse, q_pos, k_pos, scale=None, q_start=None):
     """Sums of absolute terms of each gradient element of one chunk.
 
     A backward that rounds P and dS to a format with unit roundoff u (and
@@ -107,6 +111,8 @@ def attention_backward_magnitudes(q, k, v, do, o, lse, q_pos, k_pos, scale=None)
     k_pos = np.asarray(k_pos, dtype=np.int64)
     sq, hq, d = q.shape
     sk, hkv, _ = k.shape
+    q_start = (np.full(sq, np.iinfo(np.int64).min, dtype=np.int64) if q_start is None
+               else np.asarray(q_start, dtype=np.int64))
     group = hq // hkv
     if scale is None:
         scale = 1.0 / np.sqrt(d)
@@ -122,10 +128,12 @@ def attention_backward_magnitudes(q, k, v, do, o, lse, q_pos, k_pos, scale=None)
         for b0 in range(0, sq, _ROWS):
             r = slice(b0, min(b0 + _ROWS, sq))
             qp = q_pos[r]
-            cols = np.nonzero(k_pos <= qp.max())[0]
+            qs = q_start[r]
+            cols = np.nonzero((k_pos <= qp.max()) & (k_pos >= qs.min()))[0]
             if cols.size == 0:
                 continue
-            vis = k_pos[cols][None, :] <= qp[:, None]
+            kc = k_pos[cols][None, :]
+            vis = (kc <= qp[:, None]) & (kc >= qs[:, None])
             l_r = lse[h, r]
             live = np.isfinite(l_r)
             s = (q[r, h, :] @ kh[cols].T) * scale

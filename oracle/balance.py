@@ -26,7 +26,21 @@ MODALITY(labels, P, g)
     total ``cum`` (ties: smaller rank first); the k-th pair goes to the k-th
     rank.  Each rank then lists its blocks in ascending order.
 
-Output layout (both modes): ``perm`` is rank-major, rank ``r``'s
+ZIGZAG_PACKED(starts, P)
+    Packed samples (variable-length videos packed into one buffer with reset
+    attention masks: same page, "Three-Stage Long-Context Alignment
+    Curriculum", stage 3, and "Critical Operational Best Practices").  A query
+    sees only its own sample, so the causal work of a sample is that of a
+    stream of its own length, and a single zigzag over the whole buffer no
+    longer balances it.  Each sample ``s`` (positions ``[starts[s],
+    starts[s+1])``, length a multiple of ``2P``, ``L_s = len / 2P``) is
+    zigzagged on its own: rank ``r`` takes its blocks ``r`` and ``2P-1-r``.
+    Rank ``r`` lists, sample by sample, its low block then its high block;
+    every rank gets ``2 L_s`` tokens and exactly equal work of every sample.
+    Also returned: ``token_start[i]``, the first position of the sample of the
+    token in slot ``i`` (the ``q_start`` of the attention with packed samples).
+
+Output layout (all modes): ``perm`` is rank-major, rank ``r``'s
 ``N / P`` global positions are ``perm[r N/P : (r+1) N/P]`` in ascending order.
 
 Why the work is exactly equal: the causal work of block ``b`` is
@@ -85,6 +99,27 @@ def modality_perm(labels, p: int, g: int) -> np.ndarray:
         for b in sorted(owned[r]):
             out.append(np.arange(b * g, (b + 1) * g))
     return np.concatenate(out).astype(np.int64)
+
+
+def zigzag_packed_perm(starts, p: int):
+    """ZIGZAG_PACKED permutation: ``(perm, token_start)``, both int64, rank-major.
+
+    ``starts``: ``n_samples + 1`` ascending positions, ``starts[0] == 0`` and
+    the last equal to ``N``; every sample length a multiple of ``2p``.
+    """
+    starts = [int(x) for x in starts]
+    if starts[0] != 0 or any(b - a <= 0 or (b - a) % (2 * p) for a, b in zip(starts, starts[1:])):
+        raise ValueError("packed zigzag needs samples of positive length divisible by 2p")
+    perm = [[] for _ in range(p)]
+    first = [[] for _ in range(p)]
+    for a, b in zip(starts, starts[1:]):
+        half = (b - a) // (2 * p)
+        for r in range(p):
+            for blk in (r, 2 * p - 1 - r):
+                perm[r].extend(range(a + blk * half, a + (blk + 1) * half))
+                first[r].extend([a] * half)
+    return (np.concatenate([np.asarray(x, dtype=np.int64) for x in perm]),
+            np.concatenate([np.asarray(x, dtype=np.int64) for x in first]))
 
 
 def inverse_perm(perm) -> np.ndarray:

@@ -44,7 +44,8 @@ def lse_merge(o_a, lse_a, o_b, lse_b):
     return o, lse
 
 
-def ring_forward(q, k_chunks, v_chunks, q_pos, k_pos_chunks, scale=None, order=None, rows=None):
+def ring_forward(q, k_chunks, v_chunks, q_pos, k_pos_chunks, scale=None, order=None, rows=None,
+                 q_start=None):
     """Attention of ``q`` against a list of KV chunks, merged chunk by chunk.
 
     ``order`` is the visiting order of the chunk indices (ring order by
@@ -58,7 +59,7 @@ def ring_forward(q, k_chunks, v_chunks, q_pos, k_pos_chunks, scale=None, order=N
     lse = None
     for c in order:
         o_c, l_c = attention_forward(q, k_chunks[c], v_chunks[c], q_pos, k_pos_chunks[c],
-                                     scale=scale, rows=rows)
+                                     scale=scale, rows=rows, q_start=q_start)
         if o is None:
             o, lse = o_c, l_c
         else:
