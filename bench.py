@@ -116,13 +116,18 @@ def build_inputs(w, device):
     return q, ks, vs, dout, labels
 
 
-def visible_pairs_per_chunk(w, perm_np, rank):
-    """Visible (q, k) pairs per query head for every chunk (host, from positions)."""
-    qp = np.sort(rank_positions(perm_np, w, rank))
+def visible_pairs_per_chunk(w, perm_np, rank, first_np=None):
+    """Visible (q, k) pairs per query head for every chunk (host, from positions;
+    with packed samples a key must also lie at or after its query's sample start)."""
+    qp = rank_positions(perm_np, w, rank)
+    qs = rank_positions(first_np, w, rank) if first_np is not None else None
     out = []
     for c in range(w.n_chunks):
         kp = np.sort(perm_np[c * w.chunk:(c + 1) * w.chunk])
-        out.append(int(np.searchsorted(kp, qp, side="right").sum()))
+        n = np.searchsorted(kp, qp, side="right")
+        if qs is not None:
+            n = n - np.searchsorted(kp, qs, side="left")
+        out.append(int(np.maximum(n, 0).sum()))
     return out
 
 
@@ -148,7 +153,7 @@ def read_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(w, rank, perm_np):
+def cpu_baseline(w, rank, perm_np, first_np=None):
     """The oracle, as it stands, on a few query heads of the workload."""
     import oracle
     from threadpoolctl import threadpool_info
@@ -168,20 +173,23 @@ def cpu_baseline(w, rank, perm_np):
     g1 = np.ascontiguousarray(gv[:, :nh, :]) if gv is not None else None
     del qv, kv, vv, gv
     qp = rank_positions(perm_np, w, rank)
+    qs_all = rank_positions(first_np, w, rank) if first_np is not None else None
     kps = [perm_np[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
     order = [(rank - t) % w.n_chunks for t in range(w.n_chunks)]
     per_pair = (4 + (10 if w.backward else 0)) * w.d * nh
     # all rows when that is at most ~30 s of oracle work, else a seeded random
     # subset of query rows (each row's work is counted exactly)
     rows = None
-    flops_all = per_pair * sum(visible_pairs_per_chunk(w, perm_np, rank))
+    pairs_all = sum(visible_pairs_per_chunk(w, perm_np, rank, first_np))
+    flops_all = per_pair * pairs_all
     if flops_all > CPU_BASELINE_FLOP_BUDGET:
         n_rows = max(64, int(w.shard * CPU_BASELINE_FLOP_BUDGET / flops_all))
         rows = np.sort(np.random.default_rng(0).choice(w.shard, n_rows, replace=False))
     qr = qp if rows is None else qp[rows]
+    qsr = None if qs_all is None else (qs_all if rows is None else qs_all[rows])
     log(f"[bench] cpu_baseline inputs ready in {time.time() - t_gen:.1f}s")
     t0 = time.time()
-    o, lse = oracle.ring_forward(q1, k1, v1, qp, kps, order=order, rows=rows)
+    o, lse = oracle.ring_forward(q1, k1, v1, qp, kps, order=order, rows=rows, q_start=qs_all)
     t_fwd = time.time() - t0
     t_bwd = 0.0
     if g1 is not None:
@@ -190,11 +198,16 @@ def cpu_baseline(w, rank, perm_np):
         q1r = q1 if rows is None else q1[rows]
         delta = oracle.bwd_delta(o, g1r)
         for c in order:
-            oracle.attention_backward(q1r, k1[c], v1[c], g1r, lse, delta, qr, kps[c])
+            oracle.attention_backward(q1r, k1[c], v1[c], g1r, lse, delta, qr, kps[c],
+                                      q_start=qsr)
         t_bwd = time.time() - t1
     pairs = 0
     for c in range(w.n_chunks):
-        pairs += int(np.searchsorted(np.sort(kps[c]), qr, side="right").sum())
+        kc = np.sort(kps[c])
+        n_vis = np.searchsorted(kc, qr, side="right")
+        if qsr is not None:
+            n_vis = n_vis - np.searchsorted(kc, qsr, side="left")
+        pairs += int(np.maximum(n_vis, 0).sum())
     flops = per_pair * pairs
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     elapsed = t_fwd + t_bwd
@@ -206,7 +219,7 @@ def cpu_baseline(w, rank, perm_np):
         "sample": (f"query heads 0-{nh - 1} of {w.hq}, "
                    + (f"all {w.shard} query rows" if rows is None else
                       f"{len(rows)} seeded random query rows of {w.shard}")
-                   + f" ({flops / (per_pair / nh * w.hq) / sum(visible_pairs_per_chunk(w, perm_np, rank)):.4f}"
+                   + f" ({flops / (per_pair / nh * w.hq) / pairs_all:.4f}"
                    f" of the step's FLOPs), all {w.n_chunks} chunks, "
                    f"forward{' + backward' if w.backward else ''}; "
                    f"fwd {t_fwd:.1f}s bwd {t_bwd:.1f}s; host affinity "
@@ -270,13 +283,18 @@ def main():
     dvs = [torch.empty(k.shape, dtype=torch.float32, device=device) for k in ks] \
         if w.backward else None
     contiguous_pos = torch.arange(n, dtype=torch.int32, device=device)
+    starts = (torch.from_numpy(w.sample_starts()).to(device) if w.layout == "packed" else None)
     timer = LaunchTimer()
     rx = ring.ChunkReceiver(ks[0], vs[0]) if args.ring_copy else None
     dk_sent = [torch.empty_like(t) for t in dks] if (rx is not None and w.backward) else None
     dv_sent = [torch.empty_like(t) for t in dvs] if (rx is not None and w.backward) else None
 
     def step(received=args.ring_copy):
-        if mode is None:  # single rank holding every position, contiguous chunks
+        first = qs = None
+        if w.layout == "packed":  # every packed sample zigzagged on its own
+            perm, _, first = mmsp.shard_balance_packed(starts, n, w.n_ranks)
+            qs = first[rank * w.shard:(rank + 1) * w.shard]
+        elif mode is None:  # single rank holding every position, contiguous chunks
             perm = contiguous_pos
         else:
             perm, _ = mmsp.shard_balance(n, w.n_ranks, mode, w.granularity,
@@ -286,18 +304,19 @@ def main():
         kps = [perm[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
         if received:
             ring.ring_forward_received(q, ks, vs, qp, kps, rx, rank=rank, fused=not args.unfused,
-                                       o=o, lse=lse, o_final=o16, timer=timer)
+                                       o=o, lse=lse, o_final=o16, timer=timer, q_start=qs)
             if w.backward:
                 ring.ring_backward_received(q, ks, vs, dout, o16, lse, qp, kps, rx, rank=rank,
                                             dq=dq, dks=dks, dvs=dvs, dk_sent=dk_sent,
-                                            dv_sent=dv_sent, delta=delta, timer=timer)
-            return perm
+                                            dv_sent=dv_sent, delta=delta, timer=timer,
+                                            q_start=qs)
+            return perm, first
         ring.ring_forward(q, ks, vs, qp, kps, rank=rank, fused=not args.unfused, o=o, lse=lse,
-                          o_final=o16, timer=timer)
+                          o_final=o16, timer=timer, q_start=qs)
         if w.backward:
             ring.ring_backward(q, ks, vs, dout, o16, lse, qp, kps, rank=rank, dq=dq, dks=dks,
-                               dvs=dvs, delta=delta, timer=timer)
-        return perm
+                               dvs=dvs, delta=delta, timer=timer, q_start=qs)
+        return perm, first
 
     def copies_only():
         """The copies one received step enqueues, without the compute."""
@@ -312,11 +331,13 @@ def main():
         rx.finish()
 
     log(f"[bench] warmup {args.warmup} steps")
-    perm = None
+    out = None
     for _ in range(args.warmup):
-        perm = step()
+        out = step()
     torch.cuda.synchronize()
-    perm_np = perm.cpu().numpy() if perm is not None else step().cpu().numpy()
+    perm, first = out if out is not None else step()
+    perm_np = perm.cpu().numpy()
+    first_np = first.cpu().numpy() if first is not None else None
 
     # timed region: barrier (one process) + synchronize on both sides
     timer.enabled = True
@@ -330,7 +351,7 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
-    pairs = visible_pairs_per_chunk(w, perm_np, rank)
+    pairs = visible_pairs_per_chunk(w, perm_np, rank, first_np)
     fwd_flops = 4.0 * d * hq * sum(pairs)
     bwd_flops = 10.0 * d * hq * sum(pairs) if w.backward else 0.0
     total_flops = fwd_flops + bwd_flops
@@ -424,7 +445,7 @@ def main():
         }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
-        result["cpu_baseline"] = cpu_baseline(w, rank, perm_np)
+        result["cpu_baseline"] = cpu_baseline(w, rank, perm_np, first_np)
     print(json.dumps(result), flush=True)
 
 

@@ -93,6 +93,34 @@ int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int3
                        int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
                        void* d_workspace, size_t workspace_bytes, void* stream);
 
+/* ---- a1 for packed samples: per-sample zigzag ------------------------------
+ * Variable-length videos packed into one buffer with reset attention masks
+ * ("LongVILA Guide ...", sections "Three-Stage Long-Context Alignment
+ * Curriculum", stage 3, and "Critical Operational Best Practices").  A query
+ * sees only keys of its own sample, so each sample is zigzagged on its own:
+ * sample s = positions [starts[s], starts[s+1]), length a positive multiple
+ * of 2*n_ranks, L_s = length/(2*n_ranks); rank r takes its blocks r and
+ * 2P-1-r.  Every rank then holds 2*L_s tokens and exactly equal causal work
+ * of every sample.
+ *
+ * d_starts      int32 [n_samples + 1] (device): 0 = starts[0] < ... <
+ *               starts[n_samples] = n.
+ * d_perm        int32 [n], rank-major: rank r's positions are
+ *               d_perm[r*n/P .. (r+1)*n/P), sample by sample, ascending.
+ * d_inv_perm    (nullable) int32 [n], d_inv_perm[d_perm[i]] = i.
+ * d_token_start (nullable) int32 [n]: starts[s] of the sample of the token
+ *               in slot i -- the q_start array of the *_packed attention
+ *               calls for any rank's shard.
+ * Host checks: n % (2*n_ranks) == 0, 1 <= n_samples <= n.  The sample
+ * boundaries live on the device and are not checked on the host: every slot
+ * is first set to -1 and tokens of a sample whose boundaries are not
+ * multiples of 2*n_ranks inside [0, n] are left unplaced (their slots keep
+ * -1).  Bit-exact integer result.
+ */
+int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_t n,
+                              int32_t n_ranks, int32_t* d_perm, int32_t* d_inv_perm,
+                              int32_t* d_token_start, void* stream);
+
 /* ---- a2: attention of the query shard against one KV chunk ---------------
  * Source: "LongVILA Guide ...", sections "Multi-Modal Sequence Parallelism
  * (MM-SP) Mechanics" (one attention kernel per ring step on the current KV
@@ -121,6 +149,21 @@ int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* o, float* lse,
                         void* stream);
+
+/* ---- a2 with packed samples -------------------------------------------------
+ * As mmsp_attn_fwd_chunk, with reset attention masks between packed samples
+ * ("LongVILA Guide ...", "Critical Operational Best Practices"): a query
+ * sees only keys of its own sample.  Samples are contiguous position ranges,
+ * so that is q_start[i] <= k_pos[j] <= q_pos[i].
+ * q_start int32 [sq] (device, required): first position of query i's sample,
+ *         q_start[i] <= q_pos[i], non-decreasing in i (as mmsp_shard_balance_
+ *         packed produces it).  flags must include MMSP_CAUSAL.
+ */
+int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
+                               const int32_t* q_pos, const int32_t* q_start,
+                               const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
+                               int32_t hkv, int32_t d, float scale, uint32_t flags, float* o,
+                               float* lse, void* stream);
 
 /* ---- a3: log-sum-exp merge of two chunk results ---------------------------
  * The page's ring loop ("Implementation ...") adds each step's output into an
@@ -168,6 +211,18 @@ int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void*
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* dq_acc, float* dk,
                         float* dv, void* stream);
+
+/* ---- a6 with packed samples -------------------------------------------------
+ * As mmsp_attn_bwd_chunk with the packed-sample visibility of
+ * mmsp_attn_fwd_chunk_packed (q_start as there; flags must include
+ * MMSP_CAUSAL); lse is the final LSE of the packed forward.
+ */
+int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, const void* dout,
+                               const float* lse, const float* delta, const int32_t* q_pos,
+                               const int32_t* q_start, const int32_t* k_pos, int32_t sq,
+                               int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
+                               uint32_t flags, float* dq_acc, float* dk, float* dv,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,81 @@ int check_attn_shapes(int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d
 
 }  // namespace
 
+namespace {
+
+int attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_pos,
+             const int32_t* q_start, const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
+             int32_t hkv, int32_t d, float scale, uint32_t flags, float* o, float* lse,
+             void* stream) {
+  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
+  const bool causal = (flags & MMSP_CAUSAL) != 0;
+  if (!q || !k || !v || !o || !lse) return MMSP_ERR_NULL;
+  if (causal && (!q_pos || !k_pos)) return MMSP_ERR_NULL;
+  const int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
+  if (st != MMSP_OK) return st;
+  mmsp::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.q_pos = q_pos;
+  p.k_pos = k_pos;
+  p.q_start = q_start;
+  p.o = o;
+  p.lse = lse;
+  p.sq = sq;
+  p.sk = sk;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  const int bm = mmsp::fwd_rows_per_block();
+  p.n_qtiles = (sq + bm - 1) / bm;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal ? 1 : 0;
+  p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
+  return check_hip(mmsp::launch_attn_fwd(p, d, as_stream(stream)));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+             const float* delta, const int32_t* q_pos, const int32_t* q_start,
+             const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d,
+             float scale, uint32_t flags, float* dq_acc, float* dk, float* dv, void* stream) {
+  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
+  const bool causal = (flags & MMSP_CAUSAL) != 0;
+  if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk || !dv) return MMSP_ERR_NULL;
+  if (causal && (!q_pos || !k_pos)) return MMSP_ERR_NULL;
+  const int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
+  if (st != MMSP_OK) return st;
+  mmsp::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.delta = delta;
+  p.q_pos = q_pos;
+  p.k_pos = k_pos;
+  p.q_start = q_start;
+  p.dq = dq_acc;
+  p.dk = dk;
+  p.dv = dv;
+  p.sq = sq;
+  p.sk = sk;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  const int bk = mmsp::bwd_keys_per_block();
+  const int bq = mmsp::bwd_rows_per_block();
+  p.n_ktiles = (sk + bk - 1) / bk;
+  p.n_qtiles = (sq + bq - 1) / bq;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal ? 1 : 0;
+  p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
+  return check_hip(mmsp::launch_attn_bwd(p, d, as_stream(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* mmsp_status_string(int status) {
@@ -80,35 +155,36 @@ int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int3
                                               as_stream(stream)));
 }
 
+int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_t n,
+                              int32_t n_ranks, int32_t* d_perm, int32_t* d_inv_perm,
+                              int32_t* d_token_start, void* stream) {
+  if (!d_starts || !d_perm) return MMSP_ERR_NULL;
+  if (n <= 0 || n > kMaxElems || n_ranks <= 0 || n_ranks > kMaxRanks || n_samples <= 0 ||
+      n_samples > n)
+    return MMSP_ERR_SHAPE;
+  if (n % (2LL * n_ranks) != 0) return MMSP_ERR_DIVISIBILITY;
+  return check_hip(mmsp::launch_shard_balance_packed(d_starts, n_samples, (int)n, n_ranks,
+                                                     d_perm, d_inv_perm, d_token_start,
+                                                     as_stream(stream)));
+}
+
 int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32_t* q_pos,
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* o, float* lse,
                         void* stream) {
-  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
-  const bool causal = (flags & MMSP_CAUSAL) != 0;
-  if (!q || !k || !v || !o || !lse) return MMSP_ERR_NULL;
-  if (causal && (!q_pos || !k_pos)) return MMSP_ERR_NULL;
-  const int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
-  if (st != MMSP_OK) return st;
-  mmsp::FwdParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.q_pos = q_pos;
-  p.k_pos = k_pos;
-  p.o = o;
-  p.lse = lse;
-  p.sq = sq;
-  p.sk = sk;
-  p.hq = hq;
-  p.hkv = hkv;
-  p.group = hq / hkv;
-  const int bm = mmsp::fwd_rows_per_block();
-  p.n_qtiles = (sq + bm - 1) / bm;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.causal = causal ? 1 : 0;
-  p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
-  return check_hip(mmsp::launch_attn_fwd(p, d, as_stream(stream)));
+  return attn_fwd(q, k, v, q_pos, nullptr, k_pos, sq, sk, hq, hkv, d, scale, flags, o, lse,
+                  stream);
+}
+
+int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
+                               const int32_t* q_pos, const int32_t* q_start,
+                               const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
+                               int32_t hkv, int32_t d, float scale, uint32_t flags, float* o,
+                               float* lse, void* stream) {
+  if (!(flags & MMSP_CAUSAL)) return MMSP_ERR_UNSUPPORTED;
+  if (!q_start) return MMSP_ERR_NULL;
+  return attn_fwd(q, k, v, q_pos, q_start, k_pos, sq, sk, hq, hkv, d, scale, flags, o, lse,
+                  stream);
 }
 
 int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
@@ -140,38 +216,20 @@ int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void*
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* dq_acc, float* dk,
                         float* dv, void* stream) {
-  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
-  const bool causal = (flags & MMSP_CAUSAL) != 0;
-  if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk || !dv) return MMSP_ERR_NULL;
-  if (causal && (!q_pos || !k_pos)) return MMSP_ERR_NULL;
-  const int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
-  if (st != MMSP_OK) return st;
-  mmsp::BwdParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.dout = static_cast<const uint16_t*>(dout);
-  p.lse = lse;
-  p.delta = delta;
-  p.q_pos = q_pos;
-  p.k_pos = k_pos;
-  p.dq = dq_acc;
-  p.dk = dk;
-  p.dv = dv;
-  p.sq = sq;
-  p.sk = sk;
-  p.hq = hq;
-  p.hkv = hkv;
-  p.group = hq / hkv;
-  const int bk = mmsp::bwd_keys_per_block();
-  const int bq = mmsp::bwd_rows_per_block();
-  p.n_ktiles = (sk + bk - 1) / bk;
-  p.n_qtiles = (sq + bq - 1) / bq;
-  p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.causal = causal ? 1 : 0;
-  p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
-  return check_hip(mmsp::launch_attn_bwd(p, d, as_stream(stream)));
+  return attn_bwd(q, k, v, dout, lse, delta, q_pos, nullptr, k_pos, sq, sk, hq, hkv, d, scale,
+                  flags, dq_acc, dk, dv, stream);
+}
+
+int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, const void* dout,
+                               const float* lse, const float* delta, const int32_t* q_pos,
+                               const int32_t* q_start, const int32_t* k_pos, int32_t sq,
+                               int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
+                               uint32_t flags, float* dq_acc, float* dk, float* dv,
+                               void* stream) {
+  if (!(flags & MMSP_CAUSAL)) return MMSP_ERR_UNSUPPORTED;
+  if (!q_start) return MMSP_ERR_NULL;
+  return attn_bwd(q, k, v, dout, lse, delta, q_pos, q_start, k_pos, sq, sk, hq, hkv, d, scale,
+                  flags, dq_acc, dk, dv, stream);
 }
 
 }  // extern "C"

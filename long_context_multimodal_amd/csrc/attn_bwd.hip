@@ -59,6 +59,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float sL[2][C::BQ];      // LSE*log2e (+inf empty)
   __shared__ __attribute__((aligned(16))) float sDl[2][C::BQ];     // delta
   __shared__ __attribute__((aligned(16))) int sQp[2][C::BQ];       // positions
+  __shared__ __attribute__((aligned(16))) int sQs[2][C::BQ];       // sample starts (packed)
   __shared__ int sQlast[2];
   auto qtile = [&](auto b) -> lds_char* {
     if constexpr (decltype(b)::value == 0) return (lds_char*)sQ0; else return (lds_char*)sQ1;
@@ -105,7 +106,20 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     }
     qstart = lo;
   }
-  const int n_qt = (p.sq + C::BQ - 1) / C::BQ;
+  // packed samples: only queries whose sample starts at or before the
+  // workgroup's last key can see it (sample starts are non-decreasing)
+  const bool packed = p.q_start != nullptr;
+  int qend = p.sq;
+  if (packed) {
+    const int kmax = p.k_pos[min(j0 + C::BK - 1, p.sk - 1)];
+    int lo = 0, hi = p.sq;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.q_start[mid] <= kmax) lo = mid + 1; else hi = mid;
+    }
+    qend = lo;
+  }
+  const int n_qt = uniform((qend + C::BQ - 1) / C::BQ);
   const int qt0 = qstart / C::BQ;
   const int per_head = n_qt - qt0;
   const int total = uniform(per_head > 0 ? per_head * p.group : 0);
@@ -163,14 +177,15 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
       ld.load_clamped(qtile(buf), p.q + o, q_row_stride, p.sq - q0);
       ld.load_clamped(otile(buf), p.dout + o, q_row_stride, p.sq - q0);
     }
-    // Per-row statistics, one array per wave (1: LSE, 2: delta, 3: positions,
-    // its lane BQ fetching the tile's last position), all into the one
-    // register `stat` from a wave-selected base.  Raw values only: they are
-    // converted when published, after the wait that ends the step, so no
-    // load here is waited for inside the step.
-    if (wave != 0 && lane <= C::BQ) {
+    // Per-row statistics, one array per wave (0: sample starts when packed,
+    // 1: LSE, 2: delta, 3: positions, its lane BQ fetching the tile's last
+    // position), all into the one register `stat` from a wave-selected base.
+    // Raw values only: they are converted when published, after the wait
+    // that ends the step, so no load here is waited for inside the step.
+    if ((wave != 0 || packed) && lane <= C::BQ) {
       const int i = min(q0 + min(lane, C::BQ - 1), p.sq - 1);
-      const uint32_t* src = wave == 1   ? (const uint32_t*)p.lse + (size_t)h * p.sq
+      const uint32_t* src = wave == 0   ? (const uint32_t*)p.q_start
+                            : wave == 1 ? (const uint32_t*)p.lse + (size_t)h * p.sq
                             : wave == 2 ? (const uint32_t*)p.delta + (size_t)h * p.sq
                             : p.causal  ? (const uint32_t*)p.q_pos
                                         : (const uint32_t*)p.lse;  // any readable row
@@ -179,7 +194,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     }
   };
   auto publish_tile = [&](int buf) {
-    if (wave == 1 && lane < C::BQ) {
+    if (wave == 0 && lane < C::BQ) {
+      sQs[buf][lane] = (packed && row_live) ? (int)stat : INT_MIN;
+    } else if (wave == 1 && lane < C::BQ) {
       // empty rows (LSE = -inf) and rows past sq get P = exp2(s c - inf) = 0
       const float l = __uint_as_float(stat);
       sL[buf][lane] = (row_live && l != -INFINITY) ? l * kLog2e : INFINITY;
@@ -208,7 +225,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     const lds_char* dt = otile(buf_tag);
     const int qfirst = uniform(sQp[BUF][0]);
     const int qlast = uniform(sQlast[BUF]);
-    if (wave_live && qlast >= wkmin) {
+    const int qs_first = uniform(sQs[BUF][0]);
+    const int qs_last = uniform(sQs[BUF][C::BQ - 1]);
+    if (wave_live && qlast >= wkmin && qs_first <= wkmax) {
       // S = Q K^T and dP = dO V^T  (row = query, col = key)
       f32x16 s = mfma32x32x16(lds_read_b128(qt, qoff[0]), kf[0], f32x16{});
       f32x16 dp = mfma32x32x16(lds_read_b128(dt, qoff[0]), lds_read_b128(vrows, qoff[0]),
@@ -219,12 +238,13 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
         dp = mfma32x32x16(lds_read_b128(dt, qoff[ks]), lds_read_b128(vrows, qoff[ks]), dp);
       }
       const int last_row_pos = uniform(sQp[BUF][C::BQ - 1]);  // INT_MIN past sq
-      if (!(wave_full_keys && qfirst >= wkmax && last_row_pos != INT_MIN)) {
+      // straddles the rows' positions or their sample starts (or the tail)
+      if (!(wave_full_keys && qfirst >= wkmax && last_row_pos != INT_MIN && qs_last <= wkmin)) {
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int q = 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (kpos > sQp[BUF][q]) s[i] = -INFINITY;
+          s[i] = ((kpos > sQp[BUF][q]) | (kpos < sQs[BUF][q])) ? -INFINITY : s[i];
         }
       }
       uint32_t pk[8], dsk[8];
@@ -373,6 +393,13 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   }
   wqmin = uniform(wqmin);
   wqmax = uniform(wqmax);
+  // packed samples: keys below a row's sample start are hidden too
+  const bool packed = p.q_start != nullptr;
+  const int qs = (packed && row_ok) ? p.q_start[row] : INT_MIN;
+  const int wqs_min = uniform((packed && wave_live) ? p.q_start[wr0] : INT_MIN);
+  const int wqs_max =
+      uniform((packed && wave_live) ? p.q_start[min(wr0 + 31, p.sq - 1)] : INT_MIN);
+  // key range of the workgroup: [kbeg, nk)
   int nk = p.sk;
   if (p.causal) {
     const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
@@ -383,7 +410,18 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
     }
     nk = lo;
   }
-  const int nt = uniform((nk + C::BN - 1) / C::BN);
+  int kbeg = 0;
+  if (packed) {
+    const int qsmin = p.q_start[q0];
+    int lo = 0, hi = p.sk;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.k_pos[mid] < qsmin) lo = mid + 1; else hi = mid;
+    }
+    kbeg = lo;
+  }
+  const int tb = uniform(kbeg / C::BN);  // first tile
+  const int nt = uniform(max(0, (nk + C::BN - 1) / C::BN - tb));
 
   // Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T
   bf16x8 qf[C::KS], df[C::KS];
@@ -418,7 +456,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   int kpreg = kPosInf;
   bool key_live = false;
   auto issue_tile = [&](int t, auto buf) {
-    const int j0 = t * C::BN;
+    const int j0 = (tb + t) * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
     if (j0 + C::BN <= p.sk) {
       ld.load(ktile(buf), kbase + o);
@@ -447,8 +485,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
     const int* kp = kpos_of(buf_tag);
     const int kfirst = uniform(kp[0]);
     const int klast = uniform(kp[C::BN - 1]);
-    if (wave_live && kfirst <= wqmax) {
-      const bool straddle = klast > wqmin;
+    if (wave_live && kfirst <= wqmax && klast >= wqs_min) {
+      // straddles the rows' positions or their sample starts
+      const bool straddle = klast > wqmin || kfirst < wqs_max;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {  // 32 keys at a time
         const int rb = kb * 32 * D * 2;
@@ -464,7 +503,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (kp[key] > qpos) s[i] = -INFINITY;
+            s[i] = ((kp[key] > qpos) | (kp[key] < qs)) ? -INFINITY : s[i];
           }
         }
         uint32_t dsk[8];

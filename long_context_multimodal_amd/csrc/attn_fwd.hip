@@ -123,6 +123,18 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   const int wqmax =
       uniform(wave_live ? (p.causal ? p.q_pos[min(wr0 + 32 * C::QB - 1, p.sq - 1)] : kPosInf - 1)
                         : INT_MIN);
+  // packed samples: keys below a row's sample start are hidden too
+  // (q_start is non-decreasing along the rows, like the positions)
+  const bool packed = p.q_start != nullptr;
+  int qs[C::QB], bqs_max[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    qs[qb] = (packed && row_ok[qb]) ? p.q_start[row[qb]] : INT_MIN;
+    const int r0 = wr0 + 32 * qb;
+    bqs_max[qb] = uniform((packed && r0 < p.sq) ? p.q_start[min(r0 + 31, p.sq - 1)] : INT_MIN);
+  }
+  const int wqs_min = uniform((packed && wave_live) ? p.q_start[wr0] : INT_MIN);
+  // key range of the workgroup: [kbeg, nk)
   int nk = p.sk;
   if (p.causal) {
     const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
@@ -133,7 +145,18 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     }
     nk = lo;
   }
-  const int nt = uniform((nk + C::BN - 1) / C::BN);
+  int kbeg = 0;
+  if (packed) {
+    const int qsmin = p.q_start[q0];
+    int lo = 0, hi = p.sk;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.k_pos[mid] < qsmin) lo = mid + 1; else hi = mid;
+    }
+    kbeg = lo;
+  }
+  const int tb = uniform(kbeg / C::BN);  // first tile
+  const int nt = uniform(max(0, (nk + C::BN - 1) / C::BN - tb));
 
   // ---- Q fragments: B operands of S^T = K Q^T (col = query, k = head dim) ----
   bf16x8 qf[C::QB][C::KS];
@@ -167,7 +190,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   typename C::Loader ld;
   ld.init(tid, kv_row_stride);
   auto issue_tile = [&](int t, auto stage) {
-    const int j0 = t * C::BN;
+    const int j0 = (tb + t) * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
     if (j0 + C::BN <= p.sk) {
       ld.load(ktile(stage), kbase + o);
@@ -209,9 +232,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     const int* kp = ptile(stage) + wave * C::BN;
     const int kfirst = uniform(kp[0]);
     const int klast = uniform(kp[C::BN - 1]);
-    const int valid = min(C::BN, p.sk - t * C::BN);
+    const int valid = min(C::BN, p.sk - (tb + t) * C::BN);
     const bool tail = valid < C::BN;
-    if (!wave_live || (causal && kfirst > wqmax)) return;
+    if (!wave_live || (causal && kfirst > wqmax) || klast < wqs_min) return;
 
     f32x16 s[C::QB][C::NKB];
 #pragma unroll
@@ -231,14 +254,16 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     uint32_t pk[C::QB][C::NKB][8];
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
-      if (tail || (causal && klast > bmin[qb])) {  // straddles this block's positions
+      // straddles this block's positions or sample starts
+      if (tail || (causal && klast > bmin[qb]) || kfirst < bqs_max[qb]) {
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool hide = (key >= valid) | (causal & (kp[key] > qpos[qb]));
+            const bool hide = (key >= valid) | (causal & (kp[key] > qpos[qb])) |
+                              (kp[key] < qs[qb]);
             s[qb][kb][i] = hide ? -INFINITY : s[qb][kb][i];
           }
       }

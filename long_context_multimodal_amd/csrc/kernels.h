@@ -13,6 +13,7 @@ struct FwdParams {
   const uint16_t* v;
   const int32_t* q_pos;
   const int32_t* k_pos;
+  const int32_t* q_start;  // packed samples: first position of each query's sample, or null
   float* o;
   float* lse;
   int sq, sk, hq, hkv, group, n_qtiles;
@@ -29,6 +30,7 @@ struct BwdParams {
   const float* delta;
   const int32_t* q_pos;
   const int32_t* k_pos;
+  const int32_t* q_start;  // packed samples: first position of each query's sample, or null
   float* dq;
   float* dk;
   float* dv;
@@ -56,5 +58,10 @@ hipError_t launch_attn_bwd(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_shard_balance(const uint8_t* labels, int n, int n_ranks, int mode, int g,
                                 int32_t* perm, int32_t* inv_perm, int32_t* ws_vis,
                                 int32_t* ws_owner, hipStream_t stream);
+
+// per-sample zigzag of packed samples (starts: n_samples + 1 positions)
+hipError_t launch_shard_balance_packed(const int32_t* starts, int n_samples, int n, int n_ranks,
+                                       int32_t* perm, int32_t* inv_perm, int32_t* token_start,
+                                       hipStream_t stream);
 
 }  // namespace mmsp

@@ -17,6 +17,16 @@
 // found by counting comparisons in parallel; (3) a scatter of every token to
 // its rank-major slot.  A rank owns exactly one low and one high block per
 // round, so a block's slot inside its rank is 2*round + (high half ? 1 : 0).
+//
+// Packed samples (variable-length videos packed with reset attention masks:
+// "LongVILA Guide ...", sections "Three-Stage Long-Context Alignment
+// Curriculum", stage 3, and "Critical Operational Best Practices"): every
+// sample is zigzagged on its own.  A token at offset o of sample s (start
+// a_s, block length L_s = len_s / 2P) lies in block b = o / L_s and goes to
+// rank b or 2P-1-b; since every earlier sample gave each rank exactly
+// 2 L_s' = len_s' / P tokens, its slot inside the rank is a_s / P + (low
+// block ? 0 : L_s) + o % L_s.  One thread per token: a fill kernel first sets
+// every slot to -1, then tokens of samples with valid boundaries are placed.
 #include "common.h"
 #include "kernels.h"
 
@@ -87,7 +97,54 @@ __global__ void __launch_bounds__(256) scatter_kernel(int n, int n_ranks, int g,
   if (inv_perm) inv_perm[pos] = idx;
 }
 
+__global__ void __launch_bounds__(256) fill_kernel(int n, int32_t* __restrict__ a,
+                                                   int32_t* __restrict__ b,
+                                                   int32_t* __restrict__ c) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  a[i] = -1;
+  if (b) b[i] = -1;
+  if (c) c[i] = -1;
+}
+
+__global__ void __launch_bounds__(256) packed_scatter_kernel(
+    int n, int n_ranks, const int32_t* __restrict__ starts, int n_samples,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ token_start) {
+  const int pos = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pos >= n) return;
+  const int P = n_ranks;
+  // sample of this position: the last s with starts[s] <= pos
+  int lo = 0, hi = n_samples;  // answer in [0, n_samples)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (starts[mid] <= pos) lo = mid; else hi = mid;
+  }
+  const int a = starts[lo], e = starts[lo + 1];
+  // boundaries must be multiples of 2P inside [0, n] with the token inside
+  if (a < 0 || e > n || a > pos || pos >= e || a % (2 * P) != 0 || e % (2 * P) != 0) return;
+  const int L = (e - a) / (2 * P);
+  const int o = pos - a;
+  const int b = o / L;
+  const int high = b >= P;
+  const int r = high ? 2 * P - 1 - b : b;
+  const int idx = r * (n / P) + a / P + (high ? L : 0) + (o - b * L);
+  perm[idx] = pos;
+  if (inv_perm) inv_perm[pos] = idx;
+  if (token_start) token_start[idx] = a;
+}
+
 }  // namespace
+
+hipError_t launch_shard_balance_packed(const int32_t* starts, int n_samples, int n, int n_ranks,
+                                       int32_t* perm, int32_t* inv_perm, int32_t* token_start,
+                                       hipStream_t stream) {
+  const dim3 grid((n + 255) / 256);
+  hipLaunchKernelGGL(fill_kernel, grid, dim3(256), 0, stream, n, perm, inv_perm, token_start);
+  hipLaunchKernelGGL(packed_scatter_kernel, grid, dim3(256), 0, stream, n, n_ranks, starts,
+                     n_samples, perm, inv_perm, token_start);
+  return hipGetLastError();
+}
 
 hipError_t launch_shard_balance(const uint8_t* labels, int n, int n_ranks, int mode, int g,
                                 int32_t* perm, int32_t* inv_perm, int32_t* ws_vis,

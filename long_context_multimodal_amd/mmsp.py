@@ -38,6 +38,12 @@ SIGNATURES = {
     "mmsp_attn_bwd_preprocess": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP]),
     "mmsp_attn_bwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
                                            _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
+    "mmsp_shard_balance_packed": (ctypes.c_int, [_VP, _I32, _I64, _I32, _VP, _VP, _VP, _VP]),
+    "mmsp_attn_fwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
+                                                  _I32, _I32, _F32, _U32, _VP, _VP, _VP]),
+    "mmsp_attn_bwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                  _I32, _I32, _I32, _I32, _I32, _F32, _U32, _VP,
+                                                  _VP, _VP, _VP]),
 }
 
 _lib = None
@@ -115,13 +121,31 @@ def shard_balance(n: int, n_ranks: int, mode: int = BALANCE_ZIGZAG, granularity:
     return perm, inv
 
 
+def shard_balance_packed(starts, n: int, n_ranks: int, with_inverse: bool = False,
+                         with_token_start: bool = True):
+    """Per-sample zigzag of packed samples (``starts`` int32[n_samples + 1] on
+    the device).  Returns ``(perm, inv_perm or None, token_start or None)``."""
+    import torch
+    _need(starts, torch.int32, "starts", 1)
+    device = starts.device
+    perm = torch.empty(n, dtype=torch.int32, device=device)
+    inv = torch.empty(n, dtype=torch.int32, device=device) if with_inverse else None
+    first = torch.empty(n, dtype=torch.int32, device=device) if with_token_start else None
+    _check(lib().mmsp_shard_balance_packed(_ptr(starts), starts.numel() - 1, n, n_ranks,
+                                           _ptr(perm), _ptr(inv), _ptr(first), _stream()),
+           "mmsp_shard_balance_packed")
+    return perm, inv, first
+
+
 # ---------------------------------------------------------------- a2
 def attn_fwd_chunk(q, k, v, q_pos=None, k_pos=None, scale=None, causal=True, o=None, lse=None,
-                   accumulate=False):
+                   accumulate=False, q_start=None):
     """Attention of ``q[sq,hq,d]`` against one chunk ``k, v[sk,hkv,d]`` (bf16).
 
     Returns ``(o fp32[sq,hq,d], lse fp32[hq,sq])``; with ``accumulate`` the
     given ``(o, lse)`` are merged with this chunk's result in place.
+    ``q_start`` (int32[sq], optional): first position of each query's packed
+    sample (reset attention masks between samples; needs ``causal``).
     """
     import torch
     _need(q, torch.bfloat16, "q", 3)
@@ -148,6 +172,15 @@ def attn_fwd_chunk(q, k, v, q_pos=None, k_pos=None, scale=None, causal=True, o=N
     _need(o, torch.float32, "o", 3)
     _need(lse, torch.float32, "lse", 2)
     flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
+    if q_start is not None:
+        _need(q_start, torch.int32, "q_start", 1)
+        if q_start.numel() != sq:
+            raise ValueError("q_start must have sq entries")
+        _check(lib().mmsp_attn_fwd_chunk_packed(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(q_pos if causal else None), _ptr(q_start),
+            _ptr(k_pos if causal else None), sq, sk, hq, hkv, d, float(scale), flags, _ptr(o),
+            _ptr(lse), _stream()), "mmsp_attn_fwd_chunk_packed")
+        return o, lse
     _check(lib().mmsp_attn_fwd_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(q_pos if causal else None),
                                      _ptr(k_pos if causal else None), sq, sk, hq, hkv, d,
                                      float(scale), flags, _ptr(o), _ptr(lse), _stream()),
@@ -194,8 +227,9 @@ def attn_bwd_preprocess(o, dout, delta=None, dq_zero=None):
 
 # ---------------------------------------------------------------- a6
 def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=None,
-                   scale=None, causal=True, accumulate=False):
-    """Backward of one chunk: adds to ``dq_acc``; returns ``(dk, dv)`` fp32."""
+                   scale=None, causal=True, accumulate=False, q_start=None):
+    """Backward of one chunk: adds to ``dq_acc``; returns ``(dk, dv)`` fp32.
+    ``q_start`` as in :func:`attn_fwd_chunk`."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, torch.bfloat16, n, 3)
@@ -214,6 +248,16 @@ def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=
     if dv is None:
         dv = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
     flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
+    if q_start is not None:
+        _need(q_start, torch.int32, "q_start", 1)
+        if q_start.numel() != sq:
+            raise ValueError("q_start must have sq entries")
+        _check(lib().mmsp_attn_bwd_chunk_packed(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
+            _ptr(q_pos if causal else None), _ptr(q_start), _ptr(k_pos if causal else None), sq,
+            sk, hq, hkv, d, float(scale), flags, _ptr(dq_acc), _ptr(dk), _ptr(dv), _stream()),
+            "mmsp_attn_bwd_chunk_packed")
+        return dk, dv
     _check(lib().mmsp_attn_bwd_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
                                      _ptr(delta), _ptr(q_pos if causal else None),
                                      _ptr(k_pos if causal else None), sq, sk, hq, hkv, d,

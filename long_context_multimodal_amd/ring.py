@@ -25,12 +25,14 @@ def ring_order(rank: int, n_chunks: int):
 
 
 def ring_forward(q, k_chunks, v_chunks, q_pos, k_pos_chunks, rank=0, fused=True, scale=None,
-                 causal=True, order=None, o_final=None, o=None, lse=None, timer=None):
+                 causal=True, order=None, o_final=None, o=None, lse=None, timer=None,
+                 q_start=None):
     """Forward over all chunks in ring order.
 
     Returns ``(o_acc fp32[sq,hq,d], lse fp32[hq,sq], o_bf16[sq,hq,d])``.  ``o``,
     ``lse`` and ``o_final`` may be given to reuse buffers; ``timer`` (optional)
     gets ``start/stop(kind, chunk)`` calls around every chunk launch.
+    ``q_start`` (optional): per-query sample starts of packed samples.
     """
     import torch
     n = len(k_chunks)
@@ -42,14 +44,14 @@ def ring_forward(q, k_chunks, v_chunks, q_pos, k_pos_chunks, rank=0, fused=True,
             timer.start("fwd", c)
         if step == 0:
             o, lse = mmsp.attn_fwd_chunk(q, k_chunks[c], v_chunks[c], q_pos, kp, scale=scale,
-                                         causal=causal, o=o, lse=lse)
+                                         causal=causal, o=o, lse=lse, q_start=q_start)
         elif fused:
             mmsp.attn_fwd_chunk(q, k_chunks[c], v_chunks[c], q_pos, kp, scale=scale,
-                                causal=causal, o=o, lse=lse, accumulate=True)
+                                causal=causal, o=o, lse=lse, accumulate=True, q_start=q_start)
         else:
             o_part, lse_part = mmsp.attn_fwd_chunk(q, k_chunks[c], v_chunks[c], q_pos, kp,
                                                    scale=scale, causal=causal, o=o_part,
-                                                   lse=lse_part)
+                                                   lse=lse_part, q_start=q_start)
             mmsp.lse_merge(o, lse, o_part, lse_part)
         if timer is not None:
             timer.stop("fwd", c)
@@ -61,7 +63,7 @@ def ring_forward(q, k_chunks, v_chunks, q_pos, k_pos_chunks, rank=0, fused=True,
 
 def ring_backward(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks, rank=0,
                   scale=None, causal=True, order=None, dq=None, dks=None, dvs=None, delta=None,
-                  timer=None):
+                  timer=None, q_start=None):
     """Backward over all chunks in ring order from the saved output and LSE.
 
     Returns ``(dq fp32[sq,hq,d], [dk_c fp32], [dv_c fp32])`` indexed by chunk.
@@ -80,7 +82,7 @@ def ring_backward(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks,
             timer.start("bwd", c)
         dks[c], dvs[c] = mmsp.attn_bwd_chunk(q, k_chunks[c], v_chunks[c], dout, lse, delta, q_pos,
                                              kp, dq, dk=dks[c], dv=dvs[c], scale=scale,
-                                             causal=causal)
+                                             causal=causal, q_start=q_start)
         if timer is not None:
             timer.stop("bwd", c)
     return dq, dks, dvs
@@ -157,7 +159,7 @@ class ChunkReceiver:
 
 def ring_forward_received(q, k_chunks, v_chunks, q_pos, k_pos_chunks, receiver, rank=0,
                           fused=True, scale=None, causal=True, o_final=None, o=None, lse=None,
-                          timer=None):
+                          timer=None, q_start=None):
     """``ring_forward`` in ring order, with every chunk after the rank's own
     arriving through ``receiver`` (a :class:`ChunkReceiver`) while the previous
     chunk is computed.  Same kernels and order, so the same results."""
@@ -177,13 +179,14 @@ def ring_forward_received(q, k_chunks, v_chunks, q_pos, k_pos_chunks, receiver, 
             timer.start("fwd", c)
         if step == 0:
             o, lse = mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale, causal=causal, o=o,
-                                         lse=lse)
+                                         lse=lse, q_start=q_start)
         elif fused:
             mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale, causal=causal, o=o, lse=lse,
-                                accumulate=True)
+                                accumulate=True, q_start=q_start)
         else:
             o_part, lse_part = mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale,
-                                                   causal=causal, o=o_part, lse=lse_part)
+                                                   causal=causal, o=o_part, lse=lse_part,
+                                                   q_start=q_start)
             mmsp.lse_merge(o, lse, o_part, lse_part)
         if timer is not None:
             timer.stop("fwd", c)
@@ -198,7 +201,8 @@ def ring_forward_received(q, k_chunks, v_chunks, q_pos, k_pos_chunks, receiver, 
 
 def ring_backward_received(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks,
                            receiver, rank=0, scale=None, causal=True, dq=None, dks=None,
-                           dvs=None, dk_sent=None, dv_sent=None, delta=None, timer=None):
+                           dvs=None, dk_sent=None, dv_sent=None, delta=None, timer=None,
+                           q_start=None):
     """``ring_backward`` with chunks arriving through ``receiver`` and each
     chunk's dK/dV sent (copied to ``dk_sent[c]``/``dv_sent[c]``) on the copy
     stream as soon as they are computed."""
@@ -221,7 +225,8 @@ def ring_backward_received(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_po
         if timer is not None:
             timer.start("bwd", c)
         dks[c], dvs[c] = mmsp.attn_bwd_chunk(q, kc, vc, dout, lse, delta, q_pos, kp, dq,
-                                             dk=dks[c], dv=dvs[c], scale=scale, causal=causal)
+                                             dk=dks[c], dv=dvs[c], scale=scale, causal=causal,
+                                             q_start=q_start)
         if timer is not None:
             timer.stop("bwd", c)
         if step > 0:

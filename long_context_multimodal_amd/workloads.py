@@ -75,13 +75,39 @@ def tiny_labels() -> np.ndarray:
                            np.zeros(384, np.uint8)])
 
 
+def packed_sample_starts(n: int, multiple: int, seed: int = SEED_SEGMENTS) -> np.ndarray:
+    """Boundaries of video samples packed into an ``n``-token buffer.
+
+    Each sample is a clip of U{2..40} frames of 576 visual tokens, each frame
+    followed by U{8..64} text tokens, its length rounded up to a multiple of
+    ``multiple`` (so every sample can be zigzagged on its own); samples are
+    drawn until the buffer is full and the last one takes the remainder.
+    ``n`` must be a multiple of ``multiple``.  Returns int32 ``[n_samples+1]``.
+    """
+    assert n % multiple == 0
+    rng = np.random.default_rng(seed)
+    starts = [0]
+    while True:
+        frames = int(rng.integers(2, 41))
+        ln = sum(FRAME_TOKENS + int(rng.integers(TEXT_RUN[0], TEXT_RUN[1] + 1))
+                 for _ in range(frames))
+        ln = -(-ln // multiple) * multiple
+        if starts[-1] + ln >= n:
+            break
+        starts.append(starts[-1] + ln)
+    starts.append(n)
+    return np.asarray(starts, dtype=np.int32)
+
+
 @dataclass(frozen=True)
 class Workload:
     """One synthetic per-rank workload.
 
     ``layout`` is ``"contiguous"`` (single rank holding every position, KV
-    split into contiguous chunks), ``"zigzag"`` or ``"modality"``; the
-    positions themselves are produced by the shard-balance step, not here.
+    split into contiguous chunks), ``"zigzag"``, ``"modality"`` or
+    ``"packed"`` (variable-length samples packed into the buffer, each
+    zigzagged on its own); the positions themselves are produced by the
+    shard-balance step, not here.
     """
 
     name: str
@@ -113,6 +139,10 @@ class Workload:
         if self.layout == "contiguous":
             return tiny_labels() if self.n_tokens == 1024 else np.zeros(self.n_tokens, np.uint8)
         return frame_text_labels(self.n_tokens)
+
+    def sample_starts(self) -> np.ndarray:
+        """Packed layout: ``n_samples + 1`` sample boundaries (int32)."""
+        return packed_sample_starts(self.n_tokens, 2 * self.n_ranks)
 
     def q(self):
         return normal_bf16(SEED_Q, (self.shard, self.hq, self.d))
@@ -153,4 +183,13 @@ ULYSSES_TRAIN = Workload("ulysses_p32_shard65536_h4_d128_fwd_bwd", 2097152, 32, 
                          "zigzag", backward=True,
                          note="as ulysses_p32_shard65536_h4_d128, forward + backward")
 
-WORKLOADS = {w.name: w for w in (TINY, RANK_FWD, GQA, MODALITY, TRAIN, ULYSSES, ULYSSES_TRAIN)}
+# Packed video samples (reset attention masks between them: same page,
+# "Critical Operational Best Practices"), per-sample zigzag over 8 ranks.
+PACKED = Workload("packed_p8_n65536_h32_d128", 65536, 8, 32, 32, 128, "packed",
+                  note="video clips of 2-40 frames packed into 65,536 tokens, each zigzagged "
+                       "over 8 ranks; rank 0 (reset masks between samples)")
+PACKED_TRAIN = Workload("packed_p8_n65536_h32_d128_fwd_bwd", 65536, 8, 32, 32, 128, "packed",
+                        backward=True, note="as packed_p8_n65536_h32_d128, forward + backward")
+
+WORKLOADS = {w.name: w for w in (TINY, RANK_FWD, GQA, MODALITY, TRAIN, ULYSSES, ULYSSES_TRAIN,
+                                 PACKED, PACKED_TRAIN)}

@@ -118,3 +118,46 @@ def test_shard_balance_rejects_and_workspace():
 def test_binding_raises_with_code():
     err = mmsp.MMSPError(-4, "where")
     assert err.code == -4 and "MMSP_ERR_DIVISIBILITY" in str(err)
+
+
+def fwd_packed(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qp=FAKE, qs=FAKE, kp=FAKE, sq=128, sk=128, hq=4, hkv=2,
+             d=128, scale=0.088, flags=1, o=FAKE, lse=FAKE)
+    a.update(kw)
+    return mmsp.lib().mmsp_attn_fwd_chunk_packed(a["q"], a["k"], a["v"], a["qp"], a["qs"],
+                                                 a["kp"], a["sq"], a["sk"], a["hq"], a["hkv"],
+                                                 a["d"], a["scale"], a["flags"], a["o"],
+                                                 a["lse"], None)
+
+
+def bwd_packed(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, lse=FAKE, delta=FAKE, qp=FAKE, qs=FAKE, kp=FAKE,
+             sq=128, sk=128, hq=4, hkv=2, d=64, scale=0.125, flags=1, dq=FAKE, dk=FAKE,
+             dv=FAKE)
+    a.update(kw)
+    return mmsp.lib().mmsp_attn_bwd_chunk_packed(
+        a["q"], a["k"], a["v"], a["do"], a["lse"], a["delta"], a["qp"], a["qs"], a["kp"],
+        a["sq"], a["sk"], a["hq"], a["hkv"], a["d"], a["scale"], a["flags"], a["dq"], a["dk"],
+        a["dv"], None)
+
+
+@pytest.mark.parametrize("fn", [fwd_packed, bwd_packed])
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=None), -1), (dict(flags=0), -3), (dict(flags=2), -3), (dict(qp=None), -1),
+    (dict(q=None), -1), (dict(sq=0), -2), (dict(d=80), -3), (dict(hq=5, hkv=2), -4),
+    (dict(flags=9), -3),
+])
+def test_packed_attention_rejects(fn, kw, code):
+    assert fn(**kw) == code
+
+
+def test_packed_shard_balance_rejects():
+    f = mmsp.lib().mmsp_shard_balance_packed
+    assert f(None, 2, 64, 4, FAKE, None, None, None) == -1
+    assert f(FAKE, 2, 64, 4, None, None, None, None) == -1
+    assert f(FAKE, 0, 64, 4, FAKE, None, None, None) == -2
+    assert f(FAKE, 65, 64, 4, FAKE, None, None, None) == -2
+    assert f(FAKE, 2, 0, 4, FAKE, None, None, None) == -2
+    assert f(FAKE, 2, 64, 0, FAKE, None, None, None) == -2
+    assert f(FAKE, 2, 64, 2048, FAKE, None, None, None) == -2
+    assert f(FAKE, 2, 60, 4, FAKE, None, None, None) == -4  # 60 % 8 != 0

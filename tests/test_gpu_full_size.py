@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 import oracle
-from long_context_multimodal_amd.workloads import (GQA, MODALITY, RANK_FWD, TRAIN, ULYSSES,
-                                                   ULYSSES_TRAIN)
+from long_context_multimodal_amd.workloads import (GQA, MODALITY, PACKED, PACKED_TRAIN, RANK_FWD,
+                                                   TRAIN, ULYSSES, ULYSSES_TRAIN)
 from tests.helpers import assert_close_abs, assert_close_rms, to_np
 
 pytestmark = pytest.mark.gpu
@@ -53,27 +53,40 @@ def _run(mm, w, backward=False, rank=0, kv_grads="full"):
     qb, qv = w.q()
     kb, kv = w.k()
     vb, vv = w.v()
-    labels = w.labels()
-    mode = mmsp.BALANCE_MODALITY if w.layout == "modality" else mmsp.BALANCE_ZIGZAG
-    perm, _ = mmsp.shard_balance(w.n_tokens, w.n_ranks, mode, w.granularity,
-                                 labels=torch.from_numpy(labels).cuda()
-                                 if mode == mmsp.BALANCE_MODALITY else None,
-                                 with_inverse=False)
-    perm_np = to_np(perm).astype(np.int64)
-    want_perm = (oracle.modality_perm(labels, w.n_ranks, w.granularity)
-                 if mode == mmsp.BALANCE_MODALITY else oracle.zigzag_perm(w.n_tokens, w.n_ranks))
+    qs = qs_np = None
+    if w.layout == "packed":
+        starts = w.sample_starts()
+        perm, _, first = mmsp.shard_balance_packed(torch.from_numpy(starts).cuda(), w.n_tokens,
+                                                   w.n_ranks)
+        perm_np = to_np(perm).astype(np.int64)
+        want_perm, want_first = oracle.zigzag_packed_perm(starts, w.n_ranks)
+        assert np.array_equal(to_np(first), want_first)  # bit-exact sample starts
+        qs = first[rank * w.shard:(rank + 1) * w.shard]
+        qs_np = want_first[rank * w.shard:(rank + 1) * w.shard]
+    else:
+        labels = w.labels()
+        mode = mmsp.BALANCE_MODALITY if w.layout == "modality" else mmsp.BALANCE_ZIGZAG
+        perm, _ = mmsp.shard_balance(w.n_tokens, w.n_ranks, mode, w.granularity,
+                                     labels=torch.from_numpy(labels).cuda()
+                                     if mode == mmsp.BALANCE_MODALITY else None,
+                                     with_inverse=False)
+        perm_np = to_np(perm).astype(np.int64)
+        want_perm = (oracle.modality_perm(labels, w.n_ranks, w.granularity)
+                     if mode == mmsp.BALANCE_MODALITY
+                     else oracle.zigzag_perm(w.n_tokens, w.n_ranks))
     assert np.array_equal(perm_np, want_perm)  # bit-exact shard permutation
     qp = perm[rank * w.shard:(rank + 1) * w.shard]
     kps = [perm[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
     q = _dev_bf16(qb)
     ks = [_dev_bf16(kb[c]) for c in range(w.n_chunks)]
     vs = [_dev_bf16(vb[c]) for c in range(w.n_chunks)]
-    o, lse, o16 = ring.ring_forward(q, ks, vs, qp, kps, rank=rank)
+    o, lse, o16 = ring.ring_forward(q, ks, vs, qp, kps, rank=rank, q_start=qs)
     out = {"o": to_np(o), "lse": to_np(lse)}
     gv = None
     if backward:
         gb, gv = w.do()
-        dq, dks, dvs = ring.ring_backward(q, ks, vs, _dev_bf16(gb), o16, lse, qp, kps, rank=rank)
+        dq, dks, dvs = ring.ring_backward(q, ks, vs, _dev_bf16(gb), o16, lse, qp, kps, rank=rank,
+                                          q_start=qs)
         out["dq"] = to_np(dq)
         if kv_grads == "full":
             out["dk"] = [to_np(t) for t in dks]
@@ -82,20 +95,21 @@ def _run(mm, w, backward=False, rank=0, kv_grads="full"):
             out["dv_sum"] = to_np(sum(t.double().sum(dim=0) for t in dvs))
         del dks, dvs
     torch.cuda.synchronize()
-    host = {"q": qv, "k": kv, "v": vv, "do": gv,
+    host = {"q": qv, "k": kv, "v": vv, "do": gv, "qs": qs_np,
             "qp": perm_np[rank * w.shard:(rank + 1) * w.shard],
             "kps": [perm_np[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)],
             "order": [(rank - t) % w.n_chunks for t in range(w.n_chunks)]}
     return out, host
 
 
-@pytest.mark.parametrize("w", [RANK_FWD, GQA, MODALITY, ULYSSES], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [RANK_FWD, GQA, MODALITY, ULYSSES, PACKED], ids=lambda w: w.name)
 def test_forward_full_size_sampled_rows(mm, w):
     out, host = _run(mm, w)
     edges = [w.granularity * k - 1 for k in range(1, 6)] + [w.granularity * k for k in range(1, 6)]
     rows = _sample_rows(w.shard, extra_edges=edges if w.granularity else ())
     o_ref, l_ref = oracle.ring_forward(host["q"], list(host["k"]), list(host["v"]), host["qp"],
-                                       host["kps"], order=host["order"], rows=rows)
+                                       host["kps"], order=host["order"], rows=rows,
+                                       q_start=None if host["qs"] is None else host["qs"])
     assert_close_abs(out["o"][rows], o_ref, what=f"{w.name} O")
     assert_close_abs(out["lse"][:, rows], l_ref, what=f"{w.name} LSE")
     # every row of a shard sees at least its own diagonal key
@@ -161,16 +175,19 @@ def _dq_rows_check(out, host, w, rows):
     """dQ (all heads) on sampled rows against the exact per-row oracle."""
     q, k, v, do = host["q"], host["k"], host["v"], host["do"]
     qp, kps, order = host["qp"], host["kps"], host["order"]
-    o_rows, l_rows = oracle.ring_forward(q, list(k), list(v), qp, kps, order=order, rows=rows)
+    qs = host["qs"]
+    qsr = None if qs is None else qs[rows]
+    o_rows, l_rows = oracle.ring_forward(q, list(k), list(v), qp, kps, order=order, rows=rows,
+                                         q_start=qs)
     assert_close_abs(out["o"][rows], o_rows, what="O rows")
     delta_rows = oracle.bwd_delta(o_rows, do[rows])
     dq_ref = np.zeros((len(rows), w.hq, w.d))
     mq_ref = np.zeros((len(rows), w.hq, w.d))
     for c in order:
         dq_c, _, _ = oracle.attention_backward(q[rows], k[c], v[c], do[rows], l_rows, delta_rows,
-                                               qp[rows], kps[c])
+                                               qp[rows], kps[c], q_start=qsr)
         mq_c, _, _ = oracle.attention_backward_magnitudes(q[rows], k[c], v[c], do[rows], o_rows,
-                                                          l_rows, qp[rows], kps[c])
+                                                          l_rows, qp[rows], kps[c], q_start=qsr)
         dq_ref += dq_c
         mq_ref += mq_c
     assert_close_rms(out["dq"][rows], dq_ref, bound=mq_ref, what="dQ rows")
@@ -183,6 +200,23 @@ def test_ulysses_training_step_full_size(mm):
     w = ULYSSES_TRAIN
     out, host = _run(mm, w, backward=True, kv_grads="dv_sum")
     rows = _sample_rows(w.shard, seed=2, n_random=8)
+    _dq_rows_check(out, host, w, rows)
+    u = 2.0 ** -9
+    do = host["do"].astype(np.float64)
+    bound = u * np.abs(do).sum(axis=0) + 1e-3
+    assert np.all(np.abs(out["dv_sum"] - do.sum(axis=0)) <= bound), "sum of dV over keys"
+
+
+def test_packed_training_step_full_size(mm):
+    """Video clips packed into 65,536 tokens, each zigzagged over 8 ranks (reset
+    masks between clips): O and dQ on sampled rows (including rows next to
+    clip boundaries), and the dV-sum identity over all keys of all chunks."""
+    w = PACKED_TRAIN
+    out, host = _run(mm, w, backward=True, kv_grads="dv_sum")
+    starts = w.sample_starts()
+    # rows whose positions sit next to a clip boundary
+    edges = np.flatnonzero(np.isin(host["qp"], np.concatenate([starts[1:-1], starts[1:-1] - 1])))
+    rows = np.unique(np.concatenate([_sample_rows(w.shard, seed=3, n_random=8), edges[:16]]))
     _dq_rows_check(out, host, w, rows)
     u = 2.0 ** -9
     do = host["do"].astype(np.float64)
