@@ -30,6 +30,9 @@ Modules:
   ring-order driver.  Pinned (split-then-merge equals unsplit).
 * :mod:`oracle.backward`  -- gradients of the chunk attention from the final
   LSE.  Pinned (central finite differences, softmax invariants).
+* :mod:`oracle.rope`      -- rotary position embedding at global positions
+  (theta = 1e7 in the 2M stage).  Pinned (hand-worked values, norms,
+  relative-position invariance, inverse).
 * :mod:`oracle.balance`   -- zigzag and modality-balanced shard
   permutations.  Pinned by closed form, invariants and brute force; the
   exact modality assignment rule is this project's definition because the
@@ -39,6 +42,7 @@ Modules:
 from .attention import attention_forward, visible_pairs  # noqa: F401
 from .merge import lse_merge, ring_forward  # noqa: F401
 from .backward import attention_backward, attention_backward_magnitudes, bwd_delta  # noqa: F401
+from .rope import rope, rope_angles, rope_bf16  # noqa: F401
 from .balance import (  # noqa: F401
     zigzag_perm,
     zigzag_packed_perm,
