@@ -61,7 +61,7 @@ class LaunchTimer:
         import torch
         self.torch = torch
         self.open = {}
-        self.done = {"fwd": [], "bwd": []}
+        self.done = {"fwd": [], "bwd": [], "rope": []}
         self.enabled = False
 
     def start(self, kind, chunk):
@@ -236,6 +236,10 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--unfused", action="store_true", help="separate merge pass per chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope-theta", type=float, default=None,
+                    help="rotate Q and every K chunk at their global positions with this rotary "
+                         "base before the ring and rotate dQ/dK back after the backward "
+                         "(one memory-bound pass each; the long-context stages use 1e7)")
     ap.add_argument("--ring-copy", action="store_true",
                     help="every KV chunk after the rank's own arrives by a device-to-device "
                          "copy on a second stream while the previous chunk is computed (dK/dV "
@@ -286,6 +290,27 @@ def main():
     starts = (torch.from_numpy(w.sample_starts()).to(device) if w.layout == "packed" else None)
     timer = LaunchTimer()
     rx = ring.ChunkReceiver(ks[0], vs[0]) if args.ring_copy else None
+    theta = args.rope_theta
+    q_rot = torch.empty_like(q) if theta else None
+    ks_rot = [torch.empty_like(t) for t in ks] if theta else None
+
+    def rope_in(qp, kps):
+        """Rotate Q and the K chunks at their positions (each K chunk once: its
+        owner rotates it before it travels)."""
+        timer.start("rope", "in")
+        mmsp.rope(q, qp, theta, out=q_rot)
+        for c in range(w.n_chunks):
+            mmsp.rope(ks[c], kps[c], theta, out=ks_rot[c])
+        timer.stop("rope", "in")
+        return q_rot, ks_rot
+
+    def rope_out(qp, kps):
+        """Gradients with respect to the unrotated Q and K."""
+        timer.start("rope", "out")
+        mmsp.rope(dq, qp, theta, inverse=True, out=dq)
+        for c in range(w.n_chunks):
+            mmsp.rope(dks[c], kps[c], theta, inverse=True, out=dks[c])
+        timer.stop("rope", "out")
     dk_sent = [torch.empty_like(t) for t in dks] if (rx is not None and w.backward) else None
     dv_sent = [torch.empty_like(t) for t in dvs] if (rx is not None and w.backward) else None
 
@@ -302,20 +327,23 @@ def main():
                                          with_inverse=False)
         qp = perm[rank * w.shard:(rank + 1) * w.shard]
         kps = [perm[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
+        qq, kk = rope_in(qp, kps) if theta else (q, ks)
         if received:
-            ring.ring_forward_received(q, ks, vs, qp, kps, rx, rank=rank, fused=not args.unfused,
+            ring.ring_forward_received(qq, kk, vs, qp, kps, rx, rank=rank, fused=not args.unfused,
                                        o=o, lse=lse, o_final=o16, timer=timer, q_start=qs)
             if w.backward:
-                ring.ring_backward_received(q, ks, vs, dout, o16, lse, qp, kps, rx, rank=rank,
+                ring.ring_backward_received(qq, kk, vs, dout, o16, lse, qp, kps, rx, rank=rank,
                                             dq=dq, dks=dks, dvs=dvs, dk_sent=dk_sent,
                                             dv_sent=dv_sent, delta=delta, timer=timer,
                                             q_start=qs)
-            return perm, first
-        ring.ring_forward(q, ks, vs, qp, kps, rank=rank, fused=not args.unfused, o=o, lse=lse,
-                          o_final=o16, timer=timer, q_start=qs)
-        if w.backward:
-            ring.ring_backward(q, ks, vs, dout, o16, lse, qp, kps, rank=rank, dq=dq, dks=dks,
-                               dvs=dvs, delta=delta, timer=timer, q_start=qs)
+        else:
+            ring.ring_forward(qq, kk, vs, qp, kps, rank=rank, fused=not args.unfused, o=o,
+                              lse=lse, o_final=o16, timer=timer, q_start=qs)
+            if w.backward:
+                ring.ring_backward(qq, kk, vs, dout, o16, lse, qp, kps, rank=rank, dq=dq, dks=dks,
+                                   dvs=dvs, delta=delta, timer=timer, q_start=qs)
+        if theta and w.backward:
+            rope_out(qp, kps)
         return perm, first
 
     def copies_only():
@@ -407,6 +435,7 @@ def main():
             "merge": "separate" if args.unfused else "fused into chunk epilogue",
             "chunks": ("received by double-buffered copies" if args.ring_copy
                        else "resident in HBM"),
+            "rope_theta": theta,
         },
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_tflops, 2) if fwd_tflops else None,
@@ -418,6 +447,15 @@ def main():
         "roofline": bwd_rf if bwd_rf is not None else fwd_rf,
         "roofline_fwd": fwd_rf,
     }
+    if theta:
+        rope_ms = sum(ms for _, ms in timer.summary("rope")) / args.steps
+        elems = (q.numel() + sum(t.numel() for t in ks)) * 2 * 2  # bf16 read + write
+        if w.backward:
+            elems += (dq.numel() + sum(t.numel() for t in dks)) * 4 * 2  # fp32 in place
+        result["rope"] = {"ms_per_step": round(rope_ms, 4),
+                          "hbm_bytes_per_step": int(elems),
+                          "GBps": round(elems / (rope_ms * 1e-3) / 1e9, 1),
+                          "share_of_step_pct": round(100 * rope_ms / ms_per_step, 2)}
     if rx is not None:
         def timed(fn):
             torch.cuda.synchronize()

@@ -224,6 +224,29 @@ int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, cons
                                uint32_t flags, float* dq_acc, float* dk, float* dv,
                                void* stream);
 
+/* ---- rotary position embedding at global positions ------------------------
+ * "LongVILA Guide ...", section "Three-Stage Long-Context Alignment
+ * Curriculum", stage 2: the rotary base theta is raised to 10,000,000 for the
+ * long-context stages.  Half-split pairs (x[i], x[i+d/2]) of the token at
+ * position pos[t] turn by the angle pos[t] * theta^(-2i/d); with inverse = 1
+ * by minus that angle (the transpose: it maps gradients with respect to the
+ * rotated queries/keys to gradients with respect to the unrotated ones).
+ *
+ * x, y   [s][h][d] of `dtype` (MMSP_DTYPE_BF16 or MMSP_DTYPE_F32); y may equal
+ *        x (in place).
+ * pos    int32 [s]: the tokens' global positions (e.g. a shard's q_pos).
+ * Angles are formed in fp64 from the integer positions; bf16 results are
+ * rounded fp64 -> fp32 -> bf16 (nearest even), fp32 results fp64 -> fp32.
+ * d in {64, 128}; theta > 1 and finite; s*h*d < 2^31.  Memory-bound, one pass.
+ * Rotate a rank's Q and its own K chunk once per layer, before the ring (the
+ * chunk then travels rotated), and apply the inverse to dQ and to each dK
+ * after the backward.
+ */
+enum { MMSP_DTYPE_BF16 = 0, MMSP_DTYPE_F32 = 1 };
+
+int mmsp_rope(const void* x, void* y, int32_t dtype, const int32_t* pos, int32_t s, int32_t h,
+              int32_t d, double theta, int32_t inverse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -232,4 +232,16 @@ int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, cons
                   flags, dq_acc, dk, dv, stream);
 }
 
+int mmsp_rope(const void* x, void* y, int32_t dtype, const int32_t* pos, int32_t s, int32_t h,
+              int32_t d, double theta, int32_t inverse, void* stream) {
+  if (!x || !y || !pos) return MMSP_ERR_NULL;
+  if (dtype != MMSP_DTYPE_BF16 && dtype != MMSP_DTYPE_F32) return MMSP_ERR_UNSUPPORTED;
+  if (inverse != 0 && inverse != 1) return MMSP_ERR_UNSUPPORTED;
+  if (bad_dim(d)) return MMSP_ERR_UNSUPPORTED;
+  if (s <= 0 || h <= 0 || (long long)s * h * d > kMaxElems) return MMSP_ERR_SHAPE;
+  if (!(theta > 1.0) || !isfinite(theta)) return MMSP_ERR_SHAPE;
+  return check_hip(mmsp::launch_rope(x, y, dtype == MMSP_DTYPE_BF16, pos, s, h, d, theta, inverse,
+                                     as_stream(stream)));
+}
+
 }  // extern "C"

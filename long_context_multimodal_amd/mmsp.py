@@ -22,6 +22,7 @@ STATUS_NAMES = {
     -4: "MMSP_ERR_DIVISIBILITY", -5: "MMSP_ERR_WORKSPACE", -6: "MMSP_ERR_HIP",
 }
 BALANCE_ZIGZAG, BALANCE_MODALITY = 0, 1
+DTYPE_BF16, DTYPE_F32 = 0, 1
 CAUSAL, ACCUMULATE = 1, 2
 
 # every symbol the header declares, with its ctypes signature
@@ -39,6 +40,8 @@ SIGNATURES = {
     "mmsp_attn_bwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
                                            _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
     "mmsp_shard_balance_packed": (ctypes.c_int, [_VP, _I32, _I64, _I32, _VP, _VP, _VP, _VP]),
+    "mmsp_rope": (ctypes.c_int, [_VP, _VP, _I32, _VP, _I32, _I32, _I32, ctypes.c_double, _I32,
+                                 _VP]),
     "mmsp_attn_fwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
                                                   _I32, _I32, _F32, _U32, _VP, _VP, _VP]),
     "mmsp_attn_bwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -264,3 +267,26 @@ def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=
                                      float(scale), flags, _ptr(dq_acc), _ptr(dk), _ptr(dv),
                                      _stream()), "mmsp_attn_bwd_chunk")
     return dk, dv
+
+
+# ---------------------------------------------------------------- rotary embedding
+def rope(x, pos, theta: float = 1.0e7, inverse: bool = False, out=None):
+    """Rotate ``x[s,h,d]`` (bf16 or fp32) at global positions ``pos`` (int32[s]).
+
+    Returns ``out`` (a new tensor unless given; ``out=x`` rotates in place).
+    """
+    import torch
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("rope: x must be bf16 or fp32")
+    _need(x, x.dtype, "x", 3)
+    _need(pos, torch.int32, "pos", 1)
+    s, h, d = x.shape
+    if pos.numel() != s:
+        raise ValueError("pos must have s entries")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, x.dtype, "out", 3)
+    dtype = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
+    _check(lib().mmsp_rope(_ptr(x), _ptr(out), dtype, _ptr(pos), s, h, d, float(theta),
+                           1 if inverse else 0, _stream()), "mmsp_rope")
+    return out

@@ -161,3 +161,19 @@ def test_packed_shard_balance_rejects():
     assert f(FAKE, 2, 64, 0, FAKE, None, None, None) == -2
     assert f(FAKE, 2, 64, 2048, FAKE, None, None, None) == -2
     assert f(FAKE, 2, 60, 4, FAKE, None, None, None) == -4  # 60 % 8 != 0
+
+
+def test_rope_rejects():
+    f = mmsp.lib().mmsp_rope
+    ok = dict(x=FAKE, y=FAKE, dt=0, pos=FAKE, s=16, h=2, d=128, theta=1e7, inv=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["y"], a["dt"], a["pos"], a["s"], a["h"], a["d"], a["theta"], a["inv"],
+                 None)
+    assert call(x=None) == -1 and call(y=None) == -1 and call(pos=None) == -1
+    assert call(dt=2) == -3 and call(inv=2) == -3 and call(d=96) == -3
+    assert call(s=0) == -2 and call(h=-1) == -2 and call(theta=1.0) == -2
+    assert call(theta=float("inf")) == -2 and call(theta=float("nan")) == -2
+    assert call(s=1 << 30, h=32) == -2
