@@ -45,7 +45,7 @@ KERNEL_SRC = {
     "attn_fwd_chunk": ("long_context_multimodal_amd/csrc/attn_fwd.hip",
                        "long_context_multimodal_amd/csrc/common.h"),
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernels_hbm_traffic_zigzag_p8_shard8192_h32_d128_fwd_bwd.txt")
 # oracle work timed for the CPU baseline, at most (about 30 s at 0.1 TFLOP/s)
 CPU_BASELINE_FLOP_BUDGET = 3.0e12
 
