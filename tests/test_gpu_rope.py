@@ -22,13 +22,15 @@ def mm():
     return mmsp, ring
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_rope_bf16_bit_exact(mm, d):
+@pytest.mark.parametrize("s,h,d", [(777, 5, 64), (777, 5, 128), (1001, 32, 128), (333, 1, 128),
+                                   (129, 4, 64), (1, 3, 128)])
+def test_rope_bf16_bit_exact(mm, s, h, d):
+    """Ragged token counts and head counts from 1 to 32 (the number of tokens a
+    block takes depends on the head count)."""
     mmsp, _ = mm
-    s, h = 777, 5
-    rng = np.random.default_rng(d)
+    rng = np.random.default_rng(d + s)
     pos = np.sort(rng.choice(2097152, s, replace=False)).astype(np.int32)
-    xb, xv = normal_bf16(90 + d, (s, h, d))
+    xb, xv = normal_bf16(90 + d + h, (s, h, d))
     x = to_dev_bf16(xb)
     y = mmsp.rope(x, to_dev_i32(pos))
     want_bits, _ = oracle.rope_bf16(xv, pos, 1e7)
@@ -40,10 +42,10 @@ def test_rope_bf16_bit_exact(mm, d):
     assert np.array_equal(to_np(x), want_bits)
 
 
-def test_rope_fp32_inverse_within_one_ulp(mm):
+@pytest.mark.parametrize("s,h,d", [(500, 3, 128), (257, 32, 64)])
+def test_rope_fp32_inverse_within_one_ulp(mm, s, h, d):
     mmsp, _ = mm
     import torch
-    s, h, d = 500, 3, 128
     rng = np.random.default_rng(3)
     pos = np.sort(rng.choice(2097152, s, replace=False)).astype(np.int32)
     x = rng.standard_normal((s, h, d)).astype(np.float32)
