@@ -48,7 +48,7 @@ struct DkdvCfg {
   static constexpr int VTILE = BK * D * 2; // bytes of the workgroup's V rows
 };
 
-template <int D>
+template <int D, bool PACKED>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   using C = DkdvCfg<D>;
   // one LDS object per pipeline buffer (the compiler then knows the direct
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   }
   // packed samples: only queries whose sample starts at or before the
   // workgroup's last key can see it (sample starts are non-decreasing)
-  const bool packed = p.q_start != nullptr;
+  constexpr bool packed = PACKED;  // q_start given
   int qend = p.sq;
   if (packed) {
     const int kmax = p.k_pos[min(j0 + C::BK - 1, p.sk - 1)];
@@ -225,8 +225,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     const lds_char* dt = otile(buf_tag);
     const int qfirst = uniform(sQp[BUF][0]);
     const int qlast = uniform(sQlast[BUF]);
-    const int qs_first = uniform(sQs[BUF][0]);
-    const int qs_last = uniform(sQs[BUF][C::BQ - 1]);
+    const int qs_first = packed ? uniform(sQs[BUF][0]) : INT_MIN;
+    const int qs_last = packed ? uniform(sQs[BUF][C::BQ - 1]) : INT_MIN;
     if (wave_live && qlast >= wkmin && qs_first <= wkmax) {
       // S = Q K^T and dP = dO V^T  (row = query, col = key)
       f32x16 s = mfma32x32x16(lds_read_b128(qt, qoff[0]), kf[0], f32x16{});
@@ -244,7 +244,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int q = 8 * (i >> 2) + 4 * hh + (i & 3);
-          s[i] = ((kpos > sQp[BUF][q]) | (kpos < sQs[BUF][q])) ? -INFINITY : s[i];
+          bool hide = kpos > sQp[BUF][q];
+          if constexpr (packed) hide |= kpos < sQs[BUF][q];
+          s[i] = hide ? -INFINITY : s[i];
         }
       }
       uint32_t pk[8], dsk[8];
@@ -343,7 +345,7 @@ struct DqCfg {
   static constexpr int TILE = BN * D * 2;
 };
 
-template <int D>
+template <int D, bool PACKED>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(16))) char sK0[C::TILE], sK1[C::TILE];
@@ -394,7 +396,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   wqmin = uniform(wqmin);
   wqmax = uniform(wqmax);
   // packed samples: keys below a row's sample start are hidden too
-  const bool packed = p.q_start != nullptr;
+  constexpr bool packed = PACKED;  // q_start given
   const int qs = (packed && row_ok) ? p.q_start[row] : INT_MIN;
   const int wqs_min = uniform((packed && wave_live) ? p.q_start[wr0] : INT_MIN);
   const int wqs_max =
@@ -559,17 +561,26 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
     }
 }
 
-template __global__ void attn_bwd_dkdv_kernel<64>(BwdParams);
-template __global__ void attn_bwd_dkdv_kernel<128>(BwdParams);
-template __global__ void attn_bwd_dq_kernel<64>(BwdParams);
-template __global__ void attn_bwd_dq_kernel<128>(BwdParams);
 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(p.n_ktiles * p.hkv), dim3(256), 0, stream, p);
+  // packed samples get their own instances so the plain causal path carries
+  // no sample-start loads, compares or bounds
+  const bool packed = p.q_start != nullptr;
+  if (packed)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3(p.n_ktiles * p.hkv), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3(p.n_ktiles * p.hkv), dim3(256), 0,
+                       stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(p.n_qtiles * p.hq), dim3(256), 0, stream, p);
+  if (packed)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), dim3(p.n_qtiles * p.hq), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), dim3(p.n_qtiles * p.hq), dim3(256), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

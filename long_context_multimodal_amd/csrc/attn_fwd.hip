@@ -57,7 +57,7 @@ struct FwdCfg {
   static constexpr int VMEM = 2 * Loader::ROUNDS + 1;  // vector-memory ops per tile per thread
 };
 
-template <int D, bool ACC>
+template <int D, bool ACC, bool PACKED>
 __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   // one LDS object per pipeline stage
@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
                         : INT_MIN);
   // packed samples: keys below a row's sample start are hidden too
   // (q_start is non-decreasing along the rows, like the positions)
-  const bool packed = p.q_start != nullptr;
+  constexpr bool packed = PACKED;  // q_start given
   int qs[C::QB], bqs_max[C::QB];
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
@@ -368,20 +368,21 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   }
 }
 
-template __global__ void attn_fwd_kernel<64, false>(FwdParams);
-template __global__ void attn_fwd_kernel<64, true>(FwdParams);
-template __global__ void attn_fwd_kernel<128, false>(FwdParams);
-template __global__ void attn_fwd_kernel<128, true>(FwdParams);
 
 template <int D>
 hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
-  const int grid = p.n_qtiles * p.hq;
-  if (p.accumulate)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, true>), dim3(grid), dim3(FwdCfg<D>::THREADS), 0,
-                       stream, p);
+  const dim3 grid(p.n_qtiles * p.hq), block(FwdCfg<D>::THREADS);
+  // packed samples get their own instances so the plain causal path carries
+  // no sample-start loads, compares or bounds
+  const bool packed = p.q_start != nullptr;
+  if (p.accumulate && packed)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, true, true>), grid, block, 0, stream, p);
+  else if (p.accumulate)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, true, false>), grid, block, 0, stream, p);
+  else if (packed)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, false, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, false>), dim3(grid), dim3(FwdCfg<D>::THREADS), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, false, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
