@@ -121,3 +121,34 @@ def test_training_step_on_rotated_queries_and_keys(mm):
         assert_close_rms(to_np(dvs[c]), bv, bound=mv, what=f"dV chunk {c}")
     assert_close_rms(to_np(dq), oracle.rope(dq_ref, qp, 1e7, inverse=True),
                      bound=_pair_sum(mq_ref), what="dQ")
+
+
+@pytest.mark.parametrize("wname", ["zigzag_p8_shard8192_h32_d128_fwd_bwd",
+                                   "ulysses_p32_shard65536_h4_d128_fwd_bwd"])
+def test_rope_full_size(mm, wname):
+    """The rotations a training step makes, at full size and in the launch
+    shape the step uses: the bf16 query shard at the rank's global positions
+    (up to 2^21 - 1 for the 2M-token shape) bit-exactly, and the fp32 inverse
+    of a gradient-sized tensor within one ulp plus the angle's fp64 error."""
+    mmsp, _ = mm
+    import torch
+    from long_context_multimodal_amd.workloads import WORKLOADS
+    w = WORKLOADS[wname]
+    pos = oracle.zigzag_perm(w.n_tokens, w.n_ranks)[:w.shard].astype(np.int32)
+    qb, qv = w.q()
+    pos_d = to_dev_i32(pos)
+    y = mmsp.rope(to_dev_bf16(qb), pos_d)
+    assert np.array_equal(to_np(y), oracle.rope_bf16(qv, pos, 1e7)[0])
+    del y
+    # an fp32 tensor of the same shape, rotated back in place
+    g = np.random.default_rng(5).standard_normal(qv.shape).astype(np.float32)
+    gd = torch.from_numpy(g).cuda()
+    mmsp.rope(gd, pos_d, inverse=True, out=gd)
+    got = to_np(gd).astype(np.float64)
+    want = oracle.rope(g, pos, 1e7, inverse=True).astype(np.float32).astype(np.float64)
+    d = w.d
+    ang = oracle.rope_angles(pos, d, 1e7)[:, None, :]
+    pair = (np.abs(g[..., :d // 2]) + np.abs(g[..., d // 2:])) * (1.0 + ang)
+    bound = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64) + \
+        8 * 2.0 ** -53 * np.concatenate([pair, pair], axis=-1)
+    assert np.all(np.abs(got - want) <= bound)
