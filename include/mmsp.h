@@ -237,7 +237,9 @@ int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, cons
  * pos    int32 [s]: the tokens' global positions (e.g. a shard's q_pos).
  * Angles are formed in fp64 from the integer positions; bf16 results are
  * rounded fp64 -> fp32 -> bf16 (nearest even), fp32 results fp64 -> fp32.
- * d in {64, 128}; theta > 1 and finite; s*h*d < 2^31.  Memory-bound, one pass.
+ * d in {64, 128} and inverse in {0, 1} (else MMSP_ERR_UNSUPPORTED); s, h >= 1,
+ * s*h*d < 2^31, theta > 1 and finite (else MMSP_ERR_SHAPE).  Memory-bound,
+ * one pass.
  * Rotate a rank's Q and its own K chunk once per layer, before the ring (the
  * chunk then travels rotated), and apply the inverse to dQ and to each dK
  * after the backward.

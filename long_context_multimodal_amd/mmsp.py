@@ -105,6 +105,13 @@ def _need(t, dtype, name, ndim=None):
     del torch
 
 
+def _shape(t, shape, name):
+    """The kernels trust the sizes they are given: every tensor they touch
+    must have exactly the shape those sizes imply."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 # ---------------------------------------------------------------- a1
 def shard_balance(n: int, n_ranks: int, mode: int = BALANCE_ZIGZAG, granularity: int = 0,
                   labels=None, with_inverse: bool = True, device="cuda"):
@@ -174,6 +181,8 @@ def attn_fwd_chunk(q, k, v, q_pos=None, k_pos=None, scale=None, causal=True, o=N
         lse = torch.empty((hq, sq), dtype=torch.float32, device=q.device)
     _need(o, torch.float32, "o", 3)
     _need(lse, torch.float32, "lse", 2)
+    _shape(o, (sq, hq, d), "o")
+    _shape(lse, (hq, sq), "lse")
     flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
     if q_start is not None:
         _need(q_start, torch.int32, "q_start", 1)
@@ -204,6 +213,12 @@ def lse_merge(o_acc, lse_acc, o_part=None, lse_part=None, o_final=None):
     _need(lse_part, torch.float32, "lse_part", 2)
     _need(o_final, torch.bfloat16, "o_final", 3)
     sq, hq, d = o_acc.shape
+    _shape(lse_acc, (hq, sq), "lse_acc")
+    _shape(o_part, (sq, hq, d), "o_part")
+    _shape(lse_part, (hq, sq), "lse_part")
+    _shape(o_final, (sq, hq, d), "o_final")
+    if (o_part is None) != (lse_part is None):
+        raise ValueError("o_part and lse_part go together")
     _check(lib().mmsp_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), sq, hq,
                                 d, _ptr(o_final), _stream()), "mmsp_lse_merge")
     return o_acc, lse_acc
@@ -220,8 +235,12 @@ def attn_bwd_preprocess(o, dout, delta=None, dq_zero=None):
     _need(dout, torch.bfloat16, "dout", 3)
     _need(dq_zero, torch.float32, "dq_zero", 3)
     sq, hq, d = o.shape
+    _shape(dout, (sq, hq, d), "dout")
+    _shape(dq_zero, (sq, hq, d), "dq_zero")
     if delta is None:
         delta = torch.empty((hq, sq), dtype=torch.float32, device=o.device)
+    _need(delta, torch.float32, "delta", 2)
+    _shape(delta, (hq, sq), "delta")
     _check(lib().mmsp_attn_bwd_preprocess(_ptr(o), _ptr(dout), sq, hq, d, _ptr(delta),
                                           _ptr(dq_zero), _stream()),
            "mmsp_attn_bwd_preprocess")
@@ -241,15 +260,27 @@ def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=
     _need(dq_acc, torch.float32, "dq_acc", 3)
     sq, hq, d = q.shape
     sk, hkv, _ = k.shape
+    _shape(k, (sk, hkv, d), "k")
+    _shape(v, (sk, hkv, d), "v")
+    _shape(dout, (sq, hq, d), "dout")
+    _shape(lse, (hq, sq), "lse")
+    _shape(delta, (hq, sq), "delta")
+    _shape(dq_acc, (sq, hq, d), "dq_acc")
     if causal:
         _need(q_pos, torch.int32, "q_pos", 1)
         _need(k_pos, torch.int32, "k_pos", 1)
+        if q_pos.numel() != sq or k_pos.numel() != sk:
+            raise ValueError("position arrays must match sq / sk")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if dk is None:
         dk = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
     if dv is None:
         dv = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
+    _need(dk, torch.float32, "dk", 3)
+    _need(dv, torch.float32, "dv", 3)
+    _shape(dk, (sk, hkv, d), "dk")
+    _shape(dv, (sk, hkv, d), "dv")
     flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
     if q_start is not None:
         _need(q_start, torch.int32, "q_start", 1)
@@ -286,6 +317,7 @@ def rope(x, pos, theta: float = 1.0e7, inverse: bool = False, out=None):
     if out is None:
         out = torch.empty_like(x)
     _need(out, x.dtype, "out", 3)
+    _shape(out, (s, h, d), "out")
     dtype = DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_F32
     _check(lib().mmsp_rope(_ptr(x), _ptr(out), dtype, _ptr(pos), s, h, d, float(theta),
                            1 if inverse else 0, _stream()), "mmsp_rope")

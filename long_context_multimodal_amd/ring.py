@@ -125,6 +125,10 @@ class ChunkReceiver:
             self.k[b].copy_(k_src, non_blocking=True)
             self.v[b].copy_(v_src, non_blocking=True)
             self.copied[b].record(self.stream)
+        # the sources are read on the copy stream: keep their memory from
+        # being reused by the caching allocator before that read is done
+        k_src.record_stream(self.stream)
+        v_src.record_stream(self.stream)
         self.bytes_received += k_src.numel() * k_src.element_size() * 2
 
     def take(self, step):
@@ -149,6 +153,8 @@ class ChunkReceiver:
         with torch.cuda.stream(self.stream):
             self.stream.wait_event(ev)
             dst.copy_(src, non_blocking=True)
+        src.record_stream(self.stream)
+        dst.record_stream(self.stream)
         self.bytes_sent += src.numel() * src.element_size()
 
     def finish(self):

@@ -51,18 +51,25 @@ def test_received_ring_matches_resident(mm, rank, fused):
     rx = ring.ChunkReceiver(ks[0], vs[0])
     dk_sent = [torch.zeros(k.shape, dtype=torch.float32, device=k.device) for k in ks]
     dv_sent = [torch.zeros(k.shape, dtype=torch.float32, device=k.device) for k in ks]
-    for _ in range(2):  # the receiver's buffers and events are reused
+    order = ring.ring_order(rank, len(ks))
+    for it in range(2):  # the receiver's buffers and events are reused
         o_b, l_b, o16_b = ring.ring_forward_received(q, ks, vs, qp, kps, rx, rank=rank,
                                                      fused=fused)
         dq_b, dk_b, dv_b = ring.ring_backward_received(q, ks, vs, do, o16_b, l_b, qp, kps, rx,
                                                        rank=rank, dk_sent=dk_sent,
                                                        dv_sent=dv_sent)
         torch.cuda.synchronize()
-        assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b) and torch.equal(o16_a, o16_b)
-        assert torch.equal(dq_a, dq_b)
-        for c in range(len(ks)):
-            assert torch.equal(dk_a[c], dk_b[c]) and torch.equal(dv_a[c], dv_b[c])
-            assert torch.equal(dk_sent[c], dk_b[c]) and torch.equal(dv_sent[c], dv_b[c])
+        # per-chunk equality first, so a mismatch names the chunk (and its
+        # receive buffer, step % 2 in ring order) that differs
+        same = {f"{name}[chunk {c}, step {order.index(c)}]": torch.equal(a[c], b[c])
+                for name, a, b in (("dK", dk_a, dk_b), ("dV", dv_a, dv_b),
+                                   ("dK sent", dk_b, dk_sent), ("dV sent", dv_b, dv_sent))
+                for c in range(len(ks))}
+        same["O"] = torch.equal(o_a, o_b) and torch.equal(o16_a, o16_b)
+        same["LSE"] = torch.equal(l_a, l_b)
+        same["dQ"] = torch.equal(dq_a, dq_b)
+        assert all(same.values()), (f"pass {it}: differs: "
+                                    f"{[k for k, v in same.items() if not v]}")
     # every chunk but the rank's own arrived through the copy stream, twice per pass
     per_chunk = ks[0].numel() * ks[0].element_size() * 2
     assert rx.bytes_received == 2 * 2 * (len(ks) - 1) * per_chunk
