@@ -505,7 +505,11 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            s[i] = ((kp[key] > qpos) | (kp[key] < qs)) ? -INFINITY : s[i];
+            if constexpr (packed)  // qs <= k_pos <= qpos as one unsigned compare
+              s[i] = ((uint32_t)kp[key] - (uint32_t)qs > (uint32_t)qpos - (uint32_t)qs)
+                         ? -INFINITY : s[i];
+            else
+              s[i] = (kp[key] > qpos) ? -INFINITY : s[i];
           }
         }
         uint32_t dsk[8];

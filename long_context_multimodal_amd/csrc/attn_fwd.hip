@@ -257,15 +257,29 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
       // straddles this block's positions or sample starts
       if (tail || (causal && klast > bmin[qb]) || kfirst < bqs_max[qb]) {
         asm volatile("" ::: "memory");
+        // visible iff lo <= k_pos <= hi: one unsigned compare of k_pos - lo
+        // against hi - lo (lo = the row's sample start, INT_MIN unless
+        // packed; hi = its position, INT_MAX without the causal mask)
+        const uint32_t lo = (uint32_t)qs[qb];
+        const uint32_t span = (uint32_t)(causal ? qpos[qb] : INT_MAX) - lo;
+        if (tail) {  // key slots past the chunk read position 0: drop them too
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
+          for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool hide = (key >= valid) | (causal & (kp[key] > qpos[qb])) |
-                              (kp[key] < qs[qb]);
-            s[qb][kb][i] = hide ? -INFINITY : s[qb][kb][i];
-          }
+            for (int i = 0; i < 16; ++i) {
+              const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+              const bool hide = ((uint32_t)kp[key] - lo > span) | (key >= valid);
+              s[qb][kb][i] = hide ? -INFINITY : s[qb][kb][i];
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+              s[qb][kb][i] = ((uint32_t)kp[key] - lo > span) ? -INFINITY : s[qb][kb][i];
+            }
+        }
       }
       float mt = -INFINITY;
 #pragma unroll
