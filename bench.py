@@ -227,6 +227,19 @@ def cpu_baseline(w, rank, perm_np, first_np=None):
     }
 
 
+def device_record(torch, mmsp):
+    """What the run was on: the peak the roofline uses is the published one
+    (2.4 GHz); the clock the runtime reports and the one reached under load
+    (see the clock counters) can differ."""
+    props = torch.cuda.get_device_properties(0)
+    info = mmsp.device_info(0)
+    return {"name": props.name, "arch": props.gcnArchName,
+            "compute_units": info["compute_units"],
+            "peak_clock_mhz": info["peak_clock_mhz"],
+            "bf16_peak_at_that_clock_tflops": round(
+                info["compute_units"] * 4096 * info["peak_clock_mhz"] * 1e6 / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,16 +380,21 @@ def main():
     perm_np = perm.cpu().numpy()
     first_np = first.cpu().numpy() if first is not None else None
 
-    # timed region: barrier (one process) + synchronize on both sides
+    # timed region: barrier (one process) + synchronize on both sides; an
+    # event between steps on the launch stream gives each step's own time
     timer.enabled = True
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     timer.enabled = False
     ms_per_step = elapsed / args.steps * 1e3
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
     pairs = visible_pairs_per_chunk(w, perm_np, rank, first_np)
@@ -401,6 +419,22 @@ def main():
                 "traffic": traffic, "avg_launch_ms": round(avg_ms, 4),
                 "launches": len(launches),
                 "algorithmic_flop_per_launch": round(tot_flop / len(launches), 1)}
+
+    def by_chunk_class(kind, per_pair):
+        """Average launch time and rate per chunk class: the rank's own chunk
+        (the causal diagonal), chunks of earlier ranks and of later ranks."""
+        out = {}
+        for cls, pick in (("own", lambda c: c == rank), ("earlier_ranks", lambda c: c < rank),
+                          ("later_ranks", lambda c: c > rank)):
+            sel = [(c, ms) for c, ms in timer.summary(kind) if pick(c)]
+            if not sel:
+                continue
+            tot_ms = sum(ms for _, ms in sel)
+            flop = sum(per_pair * d * hq * pairs[c] for c, _ in sel)
+            out[cls] = {"avg_launch_ms": round(tot_ms / len(sel), 4),
+                        "tflops": round(flop / (tot_ms * 1e-3) / 1e12, 2) if tot_ms else None,
+                        "launches": len(sel)}
+        return out
 
     fwd_rf = kernel_roofline("fwd", 4)
     bwd_rf = kernel_roofline("bwd", 10) if w.backward else None
@@ -446,6 +480,11 @@ def main():
         "visible_pairs_per_head": int(sum(pairs)),
         "roofline": bwd_rf if bwd_rf is not None else fwd_rf,
         "roofline_fwd": fwd_rf,
+        "step_ms": {"min": round(step_ms[0], 4), "median": round(step_ms[len(step_ms) // 2], 4),
+                    "max": round(step_ms[-1], 4)},
+        "chunk_classes": {"fwd": by_chunk_class("fwd", 4),
+                          **({"bwd": by_chunk_class("bwd", 10)} if w.backward else {})},
+        "device": device_record(torch, mmsp),
     }
     if theta:
         rope_ms = sum(ms for _, ms in timer.summary("rope")) / args.steps

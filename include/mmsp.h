@@ -64,6 +64,12 @@ const char* mmsp_status_string(int status);
 int mmsp_abi_version(void);
 #define MMSP_ABI_VERSION 1
 
+/* Compute units, peak shader clock (kHz) and L2 size (bytes, per XCD on a
+ * multi-die part) of a device, as the HIP runtime reports them; used to state
+ * the clock a measurement could reach.  Host-only query, no launch. */
+int mmsp_device_info(int32_t device, int32_t* compute_units, int32_t* peak_clock_khz,
+                     int32_t* l2_bytes);
+
 /* ---- a1: shard balance ---------------------------------------------------
  * Permutation of an n-token stream into n_ranks shards of equal causal work
  * (query position p attends to p+1 keys).  Problem statement: "LongVILA

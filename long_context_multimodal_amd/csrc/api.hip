@@ -123,6 +123,20 @@ const char* mmsp_status_string(int status) {
 
 int mmsp_abi_version(void) { return MMSP_ABI_VERSION; }
 
+int mmsp_device_info(int32_t device, int32_t* compute_units, int32_t* peak_clock_khz,
+                     int32_t* l2_bytes) {
+  if (!compute_units || !peak_clock_khz || !l2_bytes) return MMSP_ERR_NULL;
+  int cu = 0, clk = 0, l2 = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      hipDeviceGetAttribute(&clk, hipDeviceAttributeClockRate, device) != hipSuccess ||
+      hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, device) != hipSuccess)
+    return MMSP_ERR_HIP;
+  *compute_units = cu;
+  *peak_clock_khz = clk;
+  *l2_bytes = l2;
+  return MMSP_OK;
+}
+
 size_t mmsp_shard_balance_workspace_bytes(int64_t n, int32_t n_ranks, int32_t mode,
                                           int32_t granularity) {
   (void)n_ranks;

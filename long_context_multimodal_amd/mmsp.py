@@ -31,6 +31,7 @@ _VP, _I32, _I64, _U32, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_in
 SIGNATURES = {
     "mmsp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mmsp_abi_version": (ctypes.c_int, []),
+    "mmsp_device_info": (ctypes.c_int, [_I32, _VP, _VP, _VP]),
     "mmsp_shard_balance_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
     "mmsp_shard_balance": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "mmsp_attn_fwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
@@ -84,6 +85,15 @@ def _check(code: int, where: str):
 def _stream():
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def device_info(device: int = 0):
+    """``{"compute_units", "peak_clock_mhz", "l2_bytes"}`` of a device."""
+    cu, clk, l2 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().mmsp_device_info(device, ctypes.byref(cu), ctypes.byref(clk), ctypes.byref(l2)),
+           "mmsp_device_info")
+    return {"compute_units": cu.value, "peak_clock_mhz": clk.value / 1000.0,
+            "l2_bytes": l2.value}
 
 
 def _ptr(t):

@@ -177,3 +177,12 @@ def test_rope_rejects():
     assert call(s=0) == -2 and call(h=-1) == -2 and call(theta=1.0) == -2
     assert call(theta=float("inf")) == -2 and call(theta=float("nan")) == -2
     assert call(s=1 << 30, h=32) == -2
+
+
+def test_device_info_rejects_null():
+    lib = mmsp.lib()
+    import ctypes
+    x = ctypes.c_int32()
+    assert lib.mmsp_device_info(0, None, ctypes.byref(x), ctypes.byref(x)) == -1  # MMSP_ERR_NULL
+    assert lib.mmsp_device_info(0, ctypes.byref(x), None, ctypes.byref(x)) == -1  # MMSP_ERR_NULL
+    assert lib.mmsp_device_info(0, ctypes.byref(x), ctypes.byref(x), None) == -1  # MMSP_ERR_NULL
