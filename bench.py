@@ -258,6 +258,10 @@ def main():
                          "copy on a second stream while the previous chunk is computed (dK/dV "
                          "copied out likewise); also times the resident ring and the copies "
                          "alone and reports the overlap loss")
+    ap.add_argument("--gather", action="store_true",
+                    help="also time moving the whole token stream ([N][hq][d] bf16) into the "
+                         "balanced rank-major order (done once at the model input, so reported "
+                         "on its own, not in the step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -520,6 +524,26 @@ def main():
             "copy_only_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
             "exposed_copy_pct": round(100 * max(0.0, ms_per_step - resident_ms) / copy_ms, 2),
         }
+    if args.gather:
+        stream = torch.empty((n, hq, d), dtype=torch.bfloat16, device=device).normal_()
+        into = torch.empty_like(stream)
+        perm_all = torch.from_numpy(perm_np.astype(np.int32)).to(device)
+        for _ in range(2):
+            mmsp.shard_gather(stream, perm_all, out=into)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(args.steps):
+            mmsp.shard_gather(stream, perm_all, out=into)
+        ev[1].record()
+        torch.cuda.synchronize()
+        g_ms = ev[0].elapsed_time(ev[1]) / args.steps
+        g_bytes = 2 * stream.numel() * stream.element_size()  # every row read and written
+        result["gather"] = {"what": "whole token stream moved into rank-major shard order",
+                            "rows": n, "row_bytes": hq * d * 2, "ms": round(g_ms, 4),
+                            "hbm_bytes": g_bytes,
+                            "GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+                            "frac_of_hbm_peak": round(g_bytes / (g_ms * 1e-3) / 8e12, 3)}
+        del stream, into
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w, rank, perm_np, first_np)

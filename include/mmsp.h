@@ -127,6 +127,24 @@ int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_
                               int32_t n_ranks, int32_t* d_perm, int32_t* d_inv_perm,
                               int32_t* d_token_start, void* stream);
 
+/* ---- a1: token rows into shard order, and back -----------------------------
+ * A rank's share of the stream is the rows its shard permutation names (the
+ * d_perm slice of mmsp_shard_balance or mmsp_shard_balance_packed).
+ * Gather:  dst[i] = src[rows[i]]  for i < n_rows  (rows[i] outside
+ *          [0, src_rows) gives a zero row, e.g. the -1 slots of unplaced
+ *          packed samples).
+ * Scatter: dst[rows[i]] = src[i]  for i < n_rows  (rows[i] outside
+ *          [0, dst_rows) is skipped); rows must be distinct, or writes race.
+ * A row is row_bytes contiguous bytes (a multiple of 16, e.g. heads * d * 2
+ * for bf16 activations); src and dst must not overlap.  n_rows, src_rows /
+ * dst_rows >= 1 and < 2^31 (else MMSP_ERR_SHAPE).  Bit-exact byte copy,
+ * memory-bound.
+ */
+int mmsp_shard_gather(const void* d_src, int64_t src_rows, const int32_t* d_rows, int64_t n_rows,
+                      int64_t row_bytes, void* d_dst, void* stream);
+int mmsp_shard_scatter(const void* d_src, int64_t n_rows, const int32_t* d_rows,
+                       int64_t dst_rows, int64_t row_bytes, void* d_dst, void* stream);
+
 /* ---- a2: attention of the query shard against one KV chunk ---------------
  * Source: "LongVILA Guide ...", sections "Multi-Modal Sequence Parallelism
  * (MM-SP) Mechanics" (one attention kernel per ring step on the current KV

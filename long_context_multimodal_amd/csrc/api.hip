@@ -182,6 +182,28 @@ int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_
                                                      as_stream(stream)));
 }
 
+namespace {
+int move_rows(const void* src, const int32_t* rows, int64_t n_rows, int64_t indexed_rows,
+              int64_t row_bytes, void* dst, bool gather, void* stream) {
+  if (!src || !rows || !dst) return MMSP_ERR_NULL;
+  if (n_rows <= 0 || indexed_rows <= 0 || n_rows > kMaxElems || indexed_rows > kMaxElems ||
+      row_bytes < 16 || row_bytes % 16 != 0 || row_bytes / 16 > kMaxElems)
+    return MMSP_ERR_SHAPE;
+  return check_hip(mmsp::launch_move_rows(src, rows, n_rows, indexed_rows, row_bytes, dst, gather,
+                                          as_stream(stream)));
+}
+}  // namespace
+
+int mmsp_shard_gather(const void* d_src, int64_t src_rows, const int32_t* d_rows, int64_t n_rows,
+                      int64_t row_bytes, void* d_dst, void* stream) {
+  return move_rows(d_src, d_rows, n_rows, src_rows, row_bytes, d_dst, true, stream);
+}
+
+int mmsp_shard_scatter(const void* d_src, int64_t n_rows, const int32_t* d_rows,
+                       int64_t dst_rows, int64_t row_bytes, void* d_dst, void* stream) {
+  return move_rows(d_src, d_rows, n_rows, dst_rows, row_bytes, d_dst, false, stream);
+}
+
 int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32_t* q_pos,
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* o, float* lse,

@@ -64,6 +64,12 @@ hipError_t launch_shard_balance_packed(const int32_t* starts, int n_samples, int
                                        int32_t* perm, int32_t* inv_perm, int32_t* token_start,
                                        hipStream_t stream);
 
+// rows of row_bytes moved by an index list: gather dst[i] = src[rows[i]],
+// scatter dst[rows[i]] = src[i]; indexed_rows bounds the indexed tensor
+hipError_t launch_move_rows(const void* src, const int32_t* rows, int64_t n_rows,
+                            int64_t indexed_rows, int64_t row_bytes, void* dst, bool gather,
+                            hipStream_t stream);
+
 // rotary embedding of a [s][h][d] bf16 or fp32 tensor (y may equal x)
 hipError_t launch_rope(const void* x, void* y, bool bf16, const int32_t* pos, int s, int h, int d,
                        double theta, int inverse, hipStream_t stream);

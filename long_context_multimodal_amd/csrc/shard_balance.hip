@@ -134,7 +134,55 @@ __global__ void __launch_bounds__(256) packed_scatter_kernel(
   if (token_start) token_start[idx] = a;
 }
 
+// Token rows moved into shard order (gather: dst[i] = src[rows[i]]) or back
+// (scatter: dst[rows[i]] = src[i]).  HBM-bound copy: one wave per row, each
+// lane moving 16-byte pieces, four in flight before the first store.  A row
+// index outside the indexed tensor gives a zero row (gather) or no write
+// (scatter) -- the -1 slots of unplaced packed samples.
+template <bool GATHER>
+__global__ void __launch_bounds__(256) move_rows_kernel(const u32x4* __restrict__ src,
+                                                        const int32_t* __restrict__ rows,
+                                                        int64_t n_rows, int64_t indexed_rows,
+                                                        int cpr, u32x4* __restrict__ dst) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_rows) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t t = rows[r];
+  const bool ok = t >= 0 && t < indexed_rows;
+  if (!GATHER && !ok) return;
+  const u32x4* sp = src + (size_t)(GATHER ? (ok ? t : 0) : r) * cpr;
+  u32x4* dp = dst + (size_t)(GATHER ? r : t) * cpr;
+  for (int c0 = lane; c0 < cpr; c0 += 64 * 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 64 * u;
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (ok && c < cpr) v[u] = sp[c];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 64 * u;
+      if (c < cpr) dp[c] = v[u];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_move_rows(const void* src, const int32_t* rows, int64_t n_rows,
+                            int64_t indexed_rows, int64_t row_bytes, void* dst, bool gather,
+                            hipStream_t stream) {
+  const int cpr = (int)(row_bytes / 16);
+  const dim3 grid((unsigned)((n_rows + 3) / 4));
+  if (gather)
+    hipLaunchKernelGGL(move_rows_kernel<true>, grid, dim3(256), 0, stream, (const u32x4*)src,
+                       rows, n_rows, indexed_rows, cpr, (u32x4*)dst);
+  else
+    hipLaunchKernelGGL(move_rows_kernel<false>, grid, dim3(256), 0, stream, (const u32x4*)src,
+                       rows, n_rows, indexed_rows, cpr, (u32x4*)dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_shard_balance_packed(const int32_t* starts, int n_samples, int n, int n_ranks,
                                        int32_t* perm, int32_t* inv_perm, int32_t* token_start,

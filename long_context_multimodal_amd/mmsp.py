@@ -41,6 +41,8 @@ SIGNATURES = {
     "mmsp_attn_bwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
                                            _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
     "mmsp_shard_balance_packed": (ctypes.c_int, [_VP, _I32, _I64, _I32, _VP, _VP, _VP, _VP]),
+    "mmsp_shard_gather": (ctypes.c_int, [_VP, _I64, _VP, _I64, _I64, _VP, _VP]),
+    "mmsp_shard_scatter": (ctypes.c_int, [_VP, _I64, _VP, _I64, _I64, _VP, _VP]),
     "mmsp_rope": (ctypes.c_int, [_VP, _VP, _I32, _VP, _I32, _I32, _I32, ctypes.c_double, _I32,
                                  _VP]),
     "mmsp_attn_fwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
@@ -155,6 +157,41 @@ def shard_balance_packed(starts, n: int, n_ranks: int, with_inverse: bool = Fals
                                            _ptr(perm), _ptr(inv), _ptr(first), _stream()),
            "mmsp_shard_balance_packed")
     return perm, inv, first
+
+
+def shard_gather(x, rows, out=None):
+    """``out[i] = x[rows[i]]`` over the first dimension (zero rows where
+    ``rows[i]`` is outside ``x``); ``rows`` int32 on the device."""
+    import torch
+    _need(rows, torch.int32, "rows", 1)
+    if x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError("x: expected a contiguous device tensor")
+    shape = (rows.numel(),) + tuple(x.shape[1:])
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or tuple(out.shape) != shape or not out.is_contiguous():
+        raise ValueError(f"out: expected a contiguous {x.dtype} tensor of shape {shape}")
+    row_bytes = x[0].numel() * x.element_size()
+    _check(lib().mmsp_shard_gather(_ptr(x), x.shape[0], _ptr(rows), rows.numel(), row_bytes,
+                                   _ptr(out), _stream()), "mmsp_shard_gather")
+    return out
+
+
+def shard_scatter(x, rows, out):
+    """``out[rows[i]] = x[i]`` over the first dimension (rows outside ``out``
+    skipped; ``rows`` distinct)."""
+    import torch
+    _need(rows, torch.int32, "rows", 1)
+    for t, n in ((x, "x"), (out, "out")):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{n}: expected a contiguous device tensor")
+    if out.dtype != x.dtype or tuple(out.shape[1:]) != tuple(x.shape[1:]) or \
+            rows.numel() != x.shape[0]:
+        raise ValueError("x, rows and out disagree")
+    row_bytes = x[0].numel() * x.element_size()
+    _check(lib().mmsp_shard_scatter(_ptr(x), x.shape[0], _ptr(rows), out.shape[0], row_bytes,
+                                    _ptr(out), _stream()), "mmsp_shard_scatter")
+    return out
 
 
 # ---------------------------------------------------------------- a2

@@ -50,4 +50,6 @@ from .balance import (  # noqa: F401
     inverse_perm,
     causal_work_per_rank,
     visual_per_rank,
+    gather_rows,
+    scatter_rows,
 )

@@ -140,3 +140,25 @@ def visual_per_rank(perm, labels, p: int) -> np.ndarray:
     """Visual-token count of each rank's shard."""
     labels = np.asarray(labels).astype(np.int64)
     return labels[np.asarray(perm, dtype=np.int64)].reshape(p, -1).sum(axis=1)
+
+
+def gather_rows(x, rows) -> np.ndarray:
+    """A rank's rows in shard order: ``out[i] = x[rows[i]]``, a zero row where
+    ``rows[i]`` does not index ``x`` (the unplaced ``-1`` slots).  The plain
+    definition of moving a token-major tensor into the balanced shard order."""
+    x = np.asarray(x)
+    out = np.zeros((len(rows),) + x.shape[1:], dtype=x.dtype)
+    for i, r in enumerate(np.asarray(rows).tolist()):
+        if 0 <= r < x.shape[0]:
+            out[i] = x[r]
+    return out
+
+
+def scatter_rows(x, rows, out) -> np.ndarray:
+    """The inverse move: ``out[rows[i]] = x[i]`` (indices outside ``out`` are
+    skipped); ``rows`` distinct.  Returns ``out``, written in place."""
+    x = np.asarray(x)
+    for i, r in enumerate(np.asarray(rows).tolist()):
+        if 0 <= r < out.shape[0]:
+            out[r] = x[i]
+    return out

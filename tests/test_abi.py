@@ -186,3 +186,17 @@ def test_device_info_rejects_null():
     assert lib.mmsp_device_info(0, None, ctypes.byref(x), ctypes.byref(x)) == -1  # MMSP_ERR_NULL
     assert lib.mmsp_device_info(0, ctypes.byref(x), None, ctypes.byref(x)) == -1  # MMSP_ERR_NULL
     assert lib.mmsp_device_info(0, ctypes.byref(x), ctypes.byref(x), None) == -1  # MMSP_ERR_NULL
+
+
+@pytest.mark.parametrize("name", ["mmsp_shard_gather", "mmsp_shard_scatter"])
+def test_shard_gather_scatter_reject(name):
+    f = getattr(mmsp.lib(), name)
+    # (src, rows_a, idx, rows_b, row_bytes, dst): the row counts swap roles
+    assert f(None, 8, FAKE, 8, 256, FAKE, None) == -1
+    assert f(FAKE, 8, None, 8, 256, FAKE, None) == -1
+    assert f(FAKE, 8, FAKE, 8, 256, None, None) == -1
+    assert f(FAKE, 0, FAKE, 8, 256, FAKE, None) == -2
+    assert f(FAKE, 8, FAKE, 0, 256, FAKE, None) == -2
+    assert f(FAKE, 8, FAKE, 8, 8, FAKE, None) == -2     # under 16 bytes
+    assert f(FAKE, 8, FAKE, 8, 264, FAKE, None) == -2   # not a multiple of 16
+    assert f(FAKE, 1 << 31, FAKE, 8, 256, FAKE, None) == -2
