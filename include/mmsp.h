@@ -127,6 +127,20 @@ int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_
                               int32_t n_ranks, int32_t* d_perm, int32_t* d_inv_perm,
                               int32_t* d_token_start, void* stream);
 
+/* ---- precondition check of positions ----------------------------------------
+ * The attention calls take position arrays as strictly increasing and packed
+ * sample starts as non-decreasing, non-negative and not after their
+ * position, without checking (a precondition: a violation gives wrong
+ * results, never an out-of-bounds access).  This call counts, on the device,
+ * the indices i that break them: pos[i] <= pos[i-1]; with d_starts (nullable)
+ * also d_starts[i] > pos[i] or < 0, and d_starts[i] < d_starts[i-1].  The
+ * count is written to d_violations (one device int32; the call zeroes it
+ * first with a kernel).  n >= 1.  For debugging; the Python binding runs it
+ * before every attention call when MMSP_CHECK_POSITIONS=1.
+ */
+int mmsp_check_positions(const int32_t* d_pos, const int32_t* d_starts, int32_t n,
+                         int32_t* d_violations, void* stream);
+
 /* ---- a1: token rows into shard order, and back -----------------------------
  * A rank's share of the stream is the rows its shard permutation names (the
  * d_perm slice of mmsp_shard_balance or mmsp_shard_balance_packed).

@@ -194,6 +194,14 @@ int move_rows(const void* src, const int32_t* rows, int64_t n_rows, int64_t inde
 }
 }  // namespace
 
+int mmsp_check_positions(const int32_t* d_pos, const int32_t* d_starts, int32_t n,
+                         int32_t* d_violations, void* stream) {
+  if (!d_pos || !d_violations) return MMSP_ERR_NULL;
+  if (n <= 0) return MMSP_ERR_SHAPE;
+  return check_hip(mmsp::launch_check_positions(d_pos, d_starts, n, d_violations,
+                                                as_stream(stream)));
+}
+
 int mmsp_shard_gather(const void* d_src, int64_t src_rows, const int32_t* d_rows, int64_t n_rows,
                       int64_t row_bytes, void* d_dst, void* stream) {
   return move_rows(d_src, d_rows, n_rows, src_rows, row_bytes, d_dst, true, stream);

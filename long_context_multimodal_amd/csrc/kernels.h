@@ -64,6 +64,10 @@ hipError_t launch_shard_balance_packed(const int32_t* starts, int n_samples, int
                                        int32_t* perm, int32_t* inv_perm, int32_t* token_start,
                                        hipStream_t stream);
 
+// counts violations of the position preconditions into *count (device)
+hipError_t launch_check_positions(const int32_t* pos, const int32_t* starts, int n,
+                                  int32_t* count, hipStream_t stream);
+
 // rows of row_bytes moved by an index list: gather dst[i] = src[rows[i]],
 // scatter dst[rows[i]] = src[i]; indexed_rows bounds the indexed tensor
 hipError_t launch_move_rows(const void* src, const int32_t* rows, int64_t n_rows,

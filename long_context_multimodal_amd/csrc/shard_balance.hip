@@ -27,6 +27,8 @@
 // 2 L_s' = len_s' / P tokens, its slot inside the rank is a_s / P + (low
 // block ? 0 : L_s) + o % L_s.  One thread per token: a fill kernel first sets
 // every slot to -1, then tokens of samples with valid boundaries are placed.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -168,7 +170,36 @@ __global__ void __launch_bounds__(256) move_rows_kernel(const u32x4* __restrict_
   }
 }
 
+// Precondition check of a position array (and of packed sample starts):
+// counts i with pos[i] <= pos[i-1], and with starts: starts[i] > pos[i],
+// starts[i] < 0 or starts[i] < starts[i-1].  One counter, zeroed by the first
+// kernel (no memset, so the pair may be captured in a graph).
+__global__ void zero_counter_kernel(int32_t* __restrict__ count) { *count = 0; }
+
+__global__ void __launch_bounds__(256) check_positions_kernel(const int32_t* __restrict__ pos,
+                                                              const int32_t* __restrict__ starts,
+                                                              int n, int32_t* __restrict__ count) {
+  int bad = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    if (i > 0 && pos[i] <= pos[i - 1]) ++bad;
+    if (starts) {
+      if (starts[i] > pos[i] || starts[i] < 0) ++bad;
+      if (i > 0 && starts[i] < starts[i - 1]) ++bad;
+    }
+  }
+  if (bad) atomicAdd(count, bad);
+}
+
 }  // namespace
+
+hipError_t launch_check_positions(const int32_t* pos, const int32_t* starts, int n,
+                                  int32_t* count, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(1), 0, stream, count);
+  const int blocks = (int)std::min<int64_t>(1024, ((int64_t)n + 255) / 256);
+  hipLaunchKernelGGL(check_positions_kernel, dim3(blocks), dim3(256), 0, stream, pos, starts, n,
+                     count);
+  return hipGetLastError();
+}
 
 hipError_t launch_move_rows(const void* src, const int32_t* rows, int64_t n_rows,
                             int64_t indexed_rows, int64_t row_bytes, void* dst, bool gather,

@@ -42,6 +42,7 @@ SIGNATURES = {
                                            _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
     "mmsp_shard_balance_packed": (ctypes.c_int, [_VP, _I32, _I64, _I32, _VP, _VP, _VP, _VP]),
     "mmsp_shard_gather": (ctypes.c_int, [_VP, _I64, _VP, _I64, _I64, _VP, _VP]),
+    "mmsp_check_positions": (ctypes.c_int, [_VP, _VP, _I32, _VP, _VP]),
     "mmsp_shard_scatter": (ctypes.c_int, [_VP, _I64, _VP, _I64, _I64, _VP, _VP]),
     "mmsp_rope": (ctypes.c_int, [_VP, _VP, _I32, _VP, _I32, _I32, _I32, ctypes.c_double, _I32,
                                  _VP]),
@@ -159,6 +160,35 @@ def shard_balance_packed(starts, n: int, n_ranks: int, with_inverse: bool = Fals
     return perm, inv, first
 
 
+CHECK_POSITIONS = os.environ.get("MMSP_CHECK_POSITIONS", "0") not in ("", "0")
+
+
+def check_positions(pos, starts=None) -> int:
+    """Number of violations of the position preconditions (strictly
+    increasing ``pos``; ``starts`` non-decreasing, non-negative, not after
+    ``pos``).  Synchronises the stream to read the count."""
+    import torch
+    _need(pos, torch.int32, "pos", 1)
+    _need(starts, torch.int32, "starts", 1)
+    if starts is not None and starts.numel() != pos.numel():
+        raise ValueError("starts must have one entry per position")
+    count = torch.empty(1, dtype=torch.int32, device=pos.device)
+    _check(lib().mmsp_check_positions(_ptr(pos), _ptr(starts), pos.numel(), _ptr(count),
+                                      _stream()), "mmsp_check_positions")
+    return int(count.item())
+
+
+def _debug_check(q_pos, k_pos, q_start):
+    """With MMSP_CHECK_POSITIONS=1: refuse position arrays the kernels would
+    read wrongly (checked on the device, one synchronisation per array)."""
+    for name, p, st in (("q_pos", q_pos, q_start), ("k_pos", k_pos, None)):
+        if p is not None:
+            bad = check_positions(p, st)
+            if bad:
+                raise ValueError(f"{name}{'/q_start' if st is not None else ''}: "
+                                 f"{bad} violations of the position preconditions")
+
+
 def shard_gather(x, rows, out=None):
     """``out[i] = x[rows[i]]`` over the first dimension (zero rows where
     ``rows[i]`` is outside ``x``); ``rows`` int32 on the device."""
@@ -230,6 +260,8 @@ def attn_fwd_chunk(q, k, v, q_pos=None, k_pos=None, scale=None, causal=True, o=N
     _need(lse, torch.float32, "lse", 2)
     _shape(o, (sq, hq, d), "o")
     _shape(lse, (hq, sq), "lse")
+    if CHECK_POSITIONS and causal:
+        _debug_check(q_pos, k_pos, q_start)
     flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
     if q_start is not None:
         _need(q_start, torch.int32, "q_start", 1)
@@ -328,6 +360,8 @@ def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=
     _need(dv, torch.float32, "dv", 3)
     _shape(dk, (sk, hkv, d), "dk")
     _shape(dv, (sk, hkv, d), "dv")
+    if CHECK_POSITIONS and causal:
+        _debug_check(q_pos, k_pos, q_start)
     flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
     if q_start is not None:
         _need(q_start, torch.int32, "q_start", 1)

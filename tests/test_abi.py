@@ -200,3 +200,10 @@ def test_shard_gather_scatter_reject(name):
     assert f(FAKE, 8, FAKE, 8, 8, FAKE, None) == -2     # under 16 bytes
     assert f(FAKE, 8, FAKE, 8, 264, FAKE, None) == -2   # not a multiple of 16
     assert f(FAKE, 1 << 31, FAKE, 8, 256, FAKE, None) == -2
+
+
+def test_check_positions_rejects():
+    f = mmsp.lib().mmsp_check_positions
+    assert f(None, None, 16, FAKE, None) == -1
+    assert f(FAKE, None, 16, None, None) == -1
+    assert f(FAKE, None, 0, FAKE, None) == -2
