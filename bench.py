@@ -227,6 +227,46 @@ def cpu_baseline(w, rank, perm_np, first_np=None):
     }
 
 
+def sdpa_context(torch, w, iters, device):
+    """PyTorch-ROCm's own flash attention (forced; no fallback to the
+    batched-matmul path) on one unmasked [1, hq, chunk, d] attention: the
+    library a user would otherwise call, timed for comparison only."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    B, H, S, D = 1, w.hq, w.chunk, w.d
+    if w.hkv != w.hq:
+        return {"skipped": "the flash backend is timed on equal query and KV heads only"}
+    try:
+        q, k, v, g = (torch.randn(B, H, S, D, device=device, dtype=torch.bfloat16)
+                      for _ in range(4))
+        for t in (q, k, v):
+            t.requires_grad_(True)
+        flop = 4.0 * D * S * S * B * H
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            for _ in range(2):
+                F.scaled_dot_product_attention(q, k, v).backward(g)
+            torch.cuda.synchronize()
+            ev[0].record()
+            for _ in range(iters):
+                F.scaled_dot_product_attention(q, k, v)
+            ev[1].record()
+            for _ in range(iters):
+                F.scaled_dot_product_attention(q, k, v).backward(g)
+            ev[2].record()
+            torch.cuda.synchronize()
+        fwd_ms = ev[0].elapsed_time(ev[1]) / iters
+        fb_ms = ev[1].elapsed_time(ev[2]) / iters
+        return {"what": f"torch.nn.functional.scaled_dot_product_attention, flash backend, "
+                        f"[{B}, {H}, {S}, {D}] bf16, no mask",
+                "torch": torch.__version__,
+                "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(flop / fwd_ms / 1e9, 1),
+                "bwd_ms": round(fb_ms - fwd_ms, 4),
+                "bwd_tflops": round(2.5 * flop / (fb_ms - fwd_ms) / 1e9, 1)}
+    except Exception as e:  # the backend may be missing on a build: context only
+        return {"skipped": f"{type(e).__name__}: {str(e)[:200]}"}
+
+
 def device_record(torch, mmsp):
     """What the run was on: the peak the roofline uses is the published one
     (2.4 GHz); the clock the runtime reports and the one reached under load
@@ -262,6 +302,10 @@ def main():
                     help="also time moving the whole token stream ([N][hq][d] bf16) into the "
                          "balanced rank-major order (done once at the model input, so reported "
                          "on its own, not in the step)")
+    ap.add_argument("--sdpa-context", action="store_true",
+                    help="also time PyTorch's scaled_dot_product_attention (flash backend only) "
+                         "on one full, unmasked chunk-sized attention [1, hq, chunk, d], forward "
+                         "and forward+backward, as third-party context (not the product path)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -544,6 +588,8 @@ def main():
                             "GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
                             "frac_of_hbm_peak": round(g_bytes / (g_ms * 1e-3) / 8e12, 3)}
         del stream, into
+    if args.sdpa_context:
+        result["sdpa_context"] = sdpa_context(torch, w, args.steps, device)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w, rank, perm_np, first_np)
