@@ -141,8 +141,10 @@ class Workload:
         return frame_text_labels(self.n_tokens)
 
     def sample_starts(self) -> np.ndarray:
-        """Packed layout: ``n_samples + 1`` sample boundaries (int32)."""
-        return packed_sample_starts(self.n_tokens, 2 * self.n_ranks)
+        """Packed layout: ``n_samples + 1`` sample boundaries (int32).  Sample
+        lengths are multiples of ``2P * granularity`` (``granularity`` 0 or 1:
+        just ``2P``, what the per-sample zigzag needs)."""
+        return packed_sample_starts(self.n_tokens, 2 * self.n_ranks * max(1, self.granularity))
 
     def q(self):
         return normal_bf16(SEED_Q, (self.shard, self.hq, self.d))
@@ -191,5 +193,13 @@ PACKED = Workload("packed_p8_n65536_h32_d128", 65536, 8, 32, 32, 128, "packed",
 PACKED_TRAIN = Workload("packed_p8_n65536_h32_d128_fwd_bwd", 65536, 8, 32, 32, 128, "packed",
                         backward=True, note="as packed_p8_n65536_h32_d128, forward + backward")
 
+# The same clips with every length rounded up to a multiple of 2P x 64, so
+# each per-rank piece is a whole number of 64-token tiles and no tile holds
+# two samples (about 4% padding tokens at this length mix).
+PACKED_ALIGNED_TRAIN = Workload("packed_aligned64_p8_n65536_h32_d128_fwd_bwd", 65536, 8, 32, 32,
+                                128, "packed", granularity=64, backward=True,
+                                note="as packed_p8_n65536_h32_d128_fwd_bwd with clip lengths "
+                                     "rounded up to multiples of 1024 (tile-aligned pieces)")
+
 WORKLOADS = {w.name: w for w in (TINY, RANK_FWD, GQA, MODALITY, TRAIN, ULYSSES, ULYSSES_TRAIN,
-                                 PACKED, PACKED_TRAIN)}
+                                 PACKED, PACKED_TRAIN, PACKED_ALIGNED_TRAIN)}
