@@ -243,7 +243,12 @@ int mmsp_attn_bwd_preprocess(const void* o, const void* dout, int32_t sq, int32_
  * dk, dv fp32 [sk][hkv][d]: overwritten, or added to with MMSP_ACCUMULATE.
  * Two kernels are enqueued on the stream (dK/dV, then dQ); the call must not
  *   overlap another call that writes the same dq_acc, dk or dv.
+ * flags MMSP_BWD_NO_DQ / MMSP_BWD_NO_DKDV enqueue only the other kernel
+ *   (dq_acc, or dk and dv, may then be NULL; both flags: MMSP_ERR_UNSUPPORTED).
+ *   The two halves read the same inputs and write disjoint outputs, so they
+ *   may run on two streams at once.
  */
+enum { MMSP_BWD_NO_DQ = 4u, MMSP_BWD_NO_DKDV = 8u };
 int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void* dout,
                         const float* lse, const float* delta, const int32_t* q_pos,
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,

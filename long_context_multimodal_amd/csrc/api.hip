@@ -69,9 +69,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* dout, cons
              const float* delta, const int32_t* q_pos, const int32_t* q_start,
              const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d,
              float scale, uint32_t flags, float* dq_acc, float* dk, float* dv, void* stream) {
-  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
+  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE | MMSP_BWD_NO_DQ | MMSP_BWD_NO_DKDV)) !=
+      0)
+    return MMSP_ERR_UNSUPPORTED;
+  const bool run_dq = (flags & MMSP_BWD_NO_DQ) == 0;
+  const bool run_dkdv = (flags & MMSP_BWD_NO_DKDV) == 0;
+  if (!run_dq && !run_dkdv) return MMSP_ERR_UNSUPPORTED;
   const bool causal = (flags & MMSP_CAUSAL) != 0;
-  if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk || !dv) return MMSP_ERR_NULL;
+  if (!q || !k || !v || !dout || !lse || !delta) return MMSP_ERR_NULL;
+  if ((run_dq && !dq_acc) || (run_dkdv && (!dk || !dv))) return MMSP_ERR_NULL;
   if (causal && (!q_pos || !k_pos)) return MMSP_ERR_NULL;
   const int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
   if (st != MMSP_OK) return st;
@@ -101,6 +107,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* dout, cons
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal ? 1 : 0;
   p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
+  p.run_dkdv = run_dkdv ? 1 : 0;
+  p.run_dq = run_dq ? 1 : 0;
   return check_hip(mmsp::launch_attn_bwd(p, d, as_stream(stream)));
 }
 

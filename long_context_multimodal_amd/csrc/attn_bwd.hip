@@ -571,14 +571,17 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   // packed samples get their own instances so the plain causal path carries
   // no sample-start loads, compares or bounds
   const bool packed = p.q_start != nullptr;
-  if (packed)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3(p.n_ktiles * p.hkv), dim3(256), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3(p.n_ktiles * p.hkv), dim3(256), 0,
-                       stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (p.run_dkdv) {
+    if (packed)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3(p.n_ktiles * p.hkv), dim3(256), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3(p.n_ktiles * p.hkv), dim3(256),
+                         0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!p.run_dq) return hipSuccess;
   if (packed)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), dim3(p.n_qtiles * p.hq), dim3(256), 0,
                        stream, p);

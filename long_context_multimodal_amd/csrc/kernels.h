@@ -38,6 +38,7 @@ struct BwdParams {
   float scale;
   float scale_log2;
   int causal, accumulate;
+  int run_dkdv, run_dq;  // which of the two kernels to enqueue
 };
 
 int fwd_rows_per_block();

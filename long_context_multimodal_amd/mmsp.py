@@ -24,6 +24,7 @@ STATUS_NAMES = {
 BALANCE_ZIGZAG, BALANCE_MODALITY = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 CAUSAL, ACCUMULATE = 1, 2
+BWD_NO_DQ, BWD_NO_DKDV = 4, 8
 
 # every symbol the header declares, with its ctypes signature
 _VP, _I32, _I64, _U32, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
@@ -328,14 +329,20 @@ def attn_bwd_preprocess(o, dout, delta=None, dq_zero=None):
 
 # ---------------------------------------------------------------- a6
 def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=None,
-                   scale=None, causal=True, accumulate=False, q_start=None):
+                   scale=None, causal=True, accumulate=False, q_start=None, part="both"):
     """Backward of one chunk: adds to ``dq_acc``; returns ``(dk, dv)`` fp32.
-    ``q_start`` as in :func:`attn_fwd_chunk`."""
+    ``q_start`` as in :func:`attn_fwd_chunk`.  ``part`` = ``"dkdv"`` or ``"dq"``
+    enqueues only that kernel (``dq_acc``, or ``dk``/``dv``, unused), so the
+    two halves can run on two streams."""
+    if part not in ("both", "dkdv", "dq"):
+        raise ValueError("part must be 'both', 'dkdv' or 'dq'")
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, torch.bfloat16, n, 3)
     _need(lse, torch.float32, "lse", 2)
     _need(delta, torch.float32, "delta", 2)
+    if part == "dkdv":
+        dq_acc = None
     _need(dq_acc, torch.float32, "dq_acc", 3)
     sq, hq, d = q.shape
     sk, hkv, _ = k.shape
@@ -352,10 +359,13 @@ def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=
             raise ValueError("position arrays must match sq / sk")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if dk is None:
-        dk = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
-    if dv is None:
-        dv = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
+    if part == "dq":
+        dk = dv = None
+    else:
+        if dk is None:
+            dk = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
+        if dv is None:
+            dv = torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device)
     _need(dk, torch.float32, "dk", 3)
     _need(dv, torch.float32, "dv", 3)
     _shape(dk, (sk, hkv, d), "dk")
@@ -363,6 +373,7 @@ def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=
     if CHECK_POSITIONS and causal:
         _debug_check(q_pos, k_pos, q_start)
     flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
+    flags |= {"both": 0, "dkdv": BWD_NO_DQ, "dq": BWD_NO_DKDV}[part]
     if q_start is not None:
         _need(q_start, torch.int32, "q_start", 1)
         if q_start.numel() != sq:

@@ -77,7 +77,10 @@ def bwd(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(do=None), -1), (dict(delta=None), -1), (dict(dq=None), -1), (dict(dv=None), -1),
-    (dict(sk=0), -2), (dict(d=32), -3), (dict(hq=7, hkv=2), -4), (dict(flags=4), -3),
+    (dict(sk=0), -2), (dict(d=32), -3), (dict(hq=7, hkv=2), -4), (dict(flags=16), -3),
+    (dict(flags=1 | 4 | 8), -3),                      # both halves skipped
+    (dict(flags=1 | 8, dq=None), -1),                 # the dQ half still needs dq_acc
+    (dict(flags=1 | 4, dv=None), -1),                 # the dK/dV half still needs dk, dv
 ])
 def test_bwd_rejects(kw, code):
     assert bwd(**kw) == code
@@ -145,7 +148,7 @@ def bwd_packed(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(qs=None), -1), (dict(flags=0), -3), (dict(flags=2), -3), (dict(qp=None), -1),
     (dict(q=None), -1), (dict(sq=0), -2), (dict(d=80), -3), (dict(hq=5, hkv=2), -4),
-    (dict(flags=9), -3),
+    (dict(flags=17), -3),  # an undefined bit
 ])
 def test_packed_attention_rejects(fn, kw, code):
     assert fn(**kw) == code

@@ -137,3 +137,39 @@ def test_tiny_training_step_chain(mm):
         assert_close_rms(to_np(dvs[c]), cc, bound=mv, what=f"dV chunk {c}")
     assert_close_rms(to_np(dq), dq_ref, bound=mq_tot, what="dQ")
     assert_close_abs(to_np(o), o_ref, what="O")
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_bwd_halves_equal_the_whole(mm, packed):
+    """``part="dkdv"`` and ``part="dq"`` enqueue one kernel each; together
+    they give bit-for-bit what one call gives, also on two streams."""
+    import torch
+    mmsp = mm[0] if isinstance(mm, tuple) else mm
+    rng = np.random.default_rng(5)
+    sq, sk, hq, hkv, d = 300, 260, 4, 2, 128
+    qp = np.sort(rng.choice(2000, sq, replace=False)).astype(np.int32)
+    kp = np.sort(rng.choice(2000, sk, replace=False)).astype(np.int32)
+    qs = np.minimum(qp, (qp // 400) * 400).astype(np.int32) if packed else None
+    dev = lambda a: torch.from_numpy(a).cuda()
+    bf = lambda *s: torch.from_numpy(rng.standard_normal(s).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    q, k, v, do = bf(sq, hq, d), bf(sk, hkv, d), bf(sk, hkv, d), bf(sq, hq, d)
+    # device tensors kept alive for the whole test: the side stream reads them
+    q_start = dev(qs) if packed else None
+    qp_d, kp_d = dev(qp), dev(kp)
+    o, lse = mmsp.attn_fwd_chunk(q, k, v, qp_d, kp_d, q_start=q_start)
+    delta = mmsp.attn_bwd_preprocess(o.to(torch.bfloat16), do)
+    dq_a = torch.zeros(sq, hq, d, device="cuda")
+    dk_a, dv_a = mmsp.attn_bwd_chunk(q, k, v, do, lse, delta, qp_d, kp_d, dq_a,
+                                     q_start=q_start)
+    dq_b = torch.zeros(sq, hq, d, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    dk_b, dv_b = mmsp.attn_bwd_chunk(q, k, v, do, lse, delta, qp_d, kp_d, None,
+                                     q_start=q_start, part="dkdv")
+    with torch.cuda.stream(side):
+        mmsp.attn_bwd_chunk(q, k, v, do, lse, delta, qp_d, kp_d, dq_b, q_start=q_start,
+                            part="dq")
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(dq_a, dq_b) and torch.equal(dk_a, dk_b) and torch.equal(dv_a, dv_b)
