@@ -142,8 +142,10 @@ int mmsp_check_positions(const int32_t* d_pos, const int32_t* d_starts, int32_t 
                          int32_t* d_violations, void* stream);
 
 /* ---- a1: token rows into shard order, and back -----------------------------
- * A rank's share of the stream is the rows its shard permutation names (the
- * d_perm slice of mmsp_shard_balance or mmsp_shard_balance_packed).
+ * Each rank holds N/P tokens of the stream ("LongVILA Guide ...", section
+ * "Multi-Modal Sequence Parallelism (MM-SP) Mechanics"); under a balance
+ * permutation those are the rows its d_perm slice names (mmsp_shard_balance
+ * or mmsp_shard_balance_packed), moved here from token order.
  * Gather:  dst[i] = src[rows[i]]  for i < n_rows  (rows[i] outside
  *          [0, src_rows) gives a zero row, e.g. the -1 slots of unplaced
  *          packed samples).

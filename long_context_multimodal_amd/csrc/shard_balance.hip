@@ -136,6 +136,8 @@ __global__ void __launch_bounds__(256) packed_scatter_kernel(
   if (token_start) token_start[idx] = a;
 }
 
+// Each rank holds N/P tokens ("LongVILA Guide ...", section "Multi-Modal
+// Sequence Parallelism (MM-SP) Mechanics"): the rows its permutation names.
 // Token rows moved into shard order (gather: dst[i] = src[rows[i]]) or back
 // (scatter: dst[rows[i]] = src[i]).  HBM-bound copy: one wave per row, each
 // lane moving 16-byte pieces, four in flight before the first store.  A row
