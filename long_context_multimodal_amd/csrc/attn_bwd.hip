@@ -162,14 +162,31 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   // qt0 .. n_qt-1.  Tiles are fetched in sequence, so the next one is tracked
   // by counters rather than recomputed with divisions.
   int nx_h = kvh * p.group, nx_q0 = qt0 * C::BQ;
+  // Running element offset of the next tile's first Q / dO element: one row
+  // block further per tile, one head further (and back to qt0) per head.
+  const size_t tile_step = (size_t)C::BQ * q_row_stride;
+  size_t nx_off = (size_t)nx_q0 * q_row_stride + (size_t)nx_h * D;
+  const size_t head_back = (size_t)(n_qt - qt0) * tile_step - D;
+  // Per-row statistics, one array per wave (0: sample starts when packed,
+  // 1: LSE, 2: delta, 3: positions, its lane BQ fetching the tile's last
+  // position), all into the one register `stat`; the array and its per-head
+  // stride are fixed per wave before the loop.
+  const uint32_t* stat_src = wave == 0   ? (const uint32_t*)p.q_start
+                             : wave == 1 ? (const uint32_t*)p.lse
+                             : wave == 2 ? (const uint32_t*)p.delta
+                             : p.causal  ? (const uint32_t*)p.q_pos
+                                         : (const uint32_t*)p.lse;  // any readable row
+  const size_t stat_head = (wave == 1 || wave == 2) ? (size_t)p.sq : 0;
   auto issue_next = [&](auto buf) {
     const int h = nx_h, q0 = nx_q0;
+    const size_t o = nx_off;
     nx_q0 += C::BQ;
+    nx_off += tile_step;
     if (nx_q0 >= n_qt * C::BQ) {
       nx_q0 = qt0 * C::BQ;
       ++nx_h;
+      nx_off -= head_back;
     }
-    const size_t o = (size_t)q0 * q_row_stride + (size_t)h * D;
     if (q0 + C::BQ <= p.sq) {
       ld.load(qtile(buf), p.q + o);
       ld.load(otile(buf), p.dout + o);
@@ -177,19 +194,11 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
       ld.load_clamped(qtile(buf), p.q + o, q_row_stride, p.sq - q0);
       ld.load_clamped(otile(buf), p.dout + o, q_row_stride, p.sq - q0);
     }
-    // Per-row statistics, one array per wave (0: sample starts when packed,
-    // 1: LSE, 2: delta, 3: positions, its lane BQ fetching the tile's last
-    // position), all into the one register `stat` from a wave-selected base.
     // Raw values only: they are converted when published, after the wait
     // that ends the step, so no load here is waited for inside the step.
     if ((wave != 0 || packed) && lane <= C::BQ) {
       const int i = min(q0 + min(lane, C::BQ - 1), p.sq - 1);
-      const uint32_t* src = wave == 0   ? (const uint32_t*)p.q_start
-                            : wave == 1 ? (const uint32_t*)p.lse + (size_t)h * p.sq
-                            : wave == 2 ? (const uint32_t*)p.delta + (size_t)h * p.sq
-                            : p.causal  ? (const uint32_t*)p.q_pos
-                                        : (const uint32_t*)p.lse;  // any readable row
-      stat = src[i];
+      stat = stat_src[(size_t)h * stat_head + i];
       row_live = q0 + lane < p.sq;
     }
   };
