@@ -410,6 +410,7 @@ def main():
     def copies_only():
         """The copies one received step enqueues, without the compute."""
         order = ring.ring_order(rank, w.n_chunks)
+        rx.start()
         for _ in range(2 if w.backward else 1):
             for t in range(1, w.n_chunks):
                 rx.receive(t, ks[order[t]], vs[order[t]])

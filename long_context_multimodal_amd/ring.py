@@ -115,6 +115,15 @@ class ChunkReceiver:
         self.bytes_received = 0
         self.bytes_sent = 0
 
+    def start(self):
+        """Order the copy stream after everything already enqueued on the
+        current stream.  Without it a copy could run ahead of that work: read
+        chunks a preceding kernel has not finished writing (a rotary pass), or
+        overwrite memory the allocator handed to the receive buffers after an
+        earlier tensor was freed while kernels still reading it were queued."""
+        import torch
+        self.stream.wait_stream(torch.cuda.current_stream())
+
     def receive(self, step, k_src, v_src):
         """Enqueue the copy of the chunk for ``step`` into buffer ``step % 2``."""
         import torch
@@ -173,6 +182,7 @@ def ring_forward_received(q, k_chunks, v_chunks, q_pos, k_pos_chunks, receiver, 
     n = len(k_chunks)
     order = ring_order(rank, n)
     o_part = lse_part = None
+    receiver.start()
     for step, c in enumerate(order):
         if step == 0:
             kc, vc = k_chunks[c], v_chunks[c]  # the rank's own chunk is local
@@ -217,6 +227,7 @@ def ring_backward_received(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_po
     order = ring_order(rank, n)
     if dq is None:
         dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    receiver.start()
     delta = mmsp.attn_bwd_preprocess(o_bf16, dout, delta, dq_zero=dq)
     dks = [None] * n if dks is None else dks
     dvs = [None] * n if dvs is None else dvs
