@@ -8,8 +8,9 @@
 //
 // Two kernels, no atomics:
 //  * dK/dV kernel -- one workgroup = 128 keys of one KV head (4 waves of 32
-//    keys).  K and V of the wave's keys stay in registers as the B operands
-//    of S = Q K^T and dP = dO V^T; the dK^T / dV^T accumulators too.  The
+//    keys).  K of the wave's keys stays in registers as the B operand of
+//    S = Q K^T, the workgroup's V rows sit in LDS as the B operand of
+//    dP = dO V^T, and the dK^T / dV^T accumulators stay in registers.  The
 //    workgroup walks the visible query tiles (32 rows) of every query head
 //    of its KV head; Q and dO tiles arrive by direct global->LDS loads into
 //    swizzled double buffers and serve both as row-major A operands (S, dP)
@@ -27,7 +28,10 @@
 //
 // Causal skipping in both: the key (or query) range of a workgroup is
 // bounded by a binary search on the sorted positions, waves skip tiles they
-// cannot see and mask only the tiles that straddle their positions.
+// cannot see and mask only the tiles that straddle their positions.  Packed
+// samples (a per-query sample start bounding the keys from below) run in
+// their own template instances.  Either kernel can be enqueued alone
+// (run_dkdv / run_dq), so a caller may put the two on separate streams.
 #include <type_traits>
 
 #include "common.h"

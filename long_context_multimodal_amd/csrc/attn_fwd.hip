@@ -28,11 +28,18 @@
 //    row sums stay in fp32 (exact LSE for the merge and the backward);
 //  * causal tile skipping from the sorted positions: a binary search bounds
 //    the key range of the workgroup, each wave skips tiles it cannot see and
-//    masks only the tiles that straddle its rows' positions (or the tail);
+//    masks only the tiles that straddle its rows' positions (or the tail),
+//    with one unsigned compare per score (sample start <= key position <=
+//    query position);
+//  * packed samples (reset masks between samples packed in one buffer) take
+//    a per-query sample start that also bounds the key range from below;
+//    they run in their own template instance, so the plain path has none of
+//    that code;
 //  * GQA: query head h reads KV head h / G; the workgroup order keeps the
-//    query heads of one KV head on one XCD (shared L2), and within a head
-//    alternates heavy and light query tiles so every XCD's share is
-//    balanced (the two zigzag blocks of a shard see different key counts).
+//    query heads of one KV head on one XCD (shared L2) and dispatches the
+//    heavier (causally longer) query tiles first; when one head's tiles span
+//    several XCDs, heavy and light tiles alternate in blocks of 8 so every
+//    XCD and shader engine gets an even share.
 #include <type_traits>
 
 #include "common.h"
