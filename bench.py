@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -132,9 +133,15 @@ def visible_pairs_per_chunk(w, perm_np, rank, first_np=None):
 
 
 def source_sha(paths):
+    """Hash of the code of the given sources: comments and whitespace are
+    dropped, so a stored counter reading stays valid across comment edits and
+    goes stale on any change to the code itself."""
     h = hashlib.sha256()
     for path in paths:
-        h.update(open(os.path.join(ROOT, path), "rb").read())
+        text = open(os.path.join(ROOT, path), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
