@@ -244,18 +244,24 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     if (!wave_live || (causal && kfirst > wqmax) || klast < wqs_min) return;
 
     f32x16 s[C::QB][C::NKB];
+    // The two 32-key halves alternate, and the scheduling groups below keep
+    // each K operand's LDS read four MFMAs ahead of its use (four reads, then
+    // one after every MFMA).  Without them the first half's reads sat right
+    // before their MFMAs, each waiting out the LDS latency.
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      const int rb = kb * 32 * D * 2;
-      bf16x8 a = lds_read_b128(kt, rb + koff[0]);
+    for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) s[qb][kb] = mfma32x32x16(a, qf[qb][0], f32x16{});
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        const bf16x8 a = lds_read_b128(kt, kb * 32 * D * 2 + koff[ks]);
 #pragma unroll
-      for (int ks = 1; ks < C::KS; ++ks) {
-        a = lds_read_b128(kt, rb + koff[ks]);
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) s[qb][kb] = mfma32x32x16(a, qf[qb][ks], s[qb][kb]);
+        for (int qb = 0; qb < C::QB; ++qb)
+          s[qb][kb] = mfma32x32x16(a, qf[qb][ks], ks == 0 ? f32x16{} : s[qb][kb]);
       }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < C::KS * C::NKB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 
     uint32_t pk[C::QB][C::NKB][8];
