@@ -234,6 +234,45 @@ def cpu_baseline(w, rank, perm_np, first_np=None):
     }
 
 
+def graph_replay(torch, step, outputs, steps):
+    """Capture one step into a HIP graph and replay it.
+
+    The graph holds the same kernels as the eager step, with the host's
+    per-launch work (argument checks, marshalling, launch calls) done once at
+    capture.  Before each checked replay the outputs are cleared eagerly, so a
+    replay that did nothing could not match; every replay must equal the eager
+    step bit for bit (the kernels are deterministic: no atomics)."""
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outputs]
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    match = True
+    for _ in range(3):
+        for t in outputs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        match = match and all(torch.equal(a, b) for a, b in zip(outputs, want))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        graph.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / steps, match
+
+
 def sdpa_context(torch, w, iters, device):
     """PyTorch-ROCm's own flash attention (forced; no fallback to the
     batched-matmul path) on one unmasked [1, hq, chunk, d] attention: the
@@ -313,9 +352,16 @@ def main():
                     help="also time PyTorch's scaled_dot_product_attention (flash backend only) "
                          "on one full, unmasked chunk-sized attention [1, hq, chunk, d], forward "
                          "and forward+backward, as third-party context (not the product path)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step into a HIP graph and time its replays (resident "
+                         "chunks only); replays are checked bit for bit against the eager step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
+    if args.graph and args.ring_copy:
+        print("--graph captures the resident-chunk step; it does not combine with --ring-copy",
+              file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring (one rank); --gpus {args.gpus} is "
               "not supported: run with --gpus 1", file=sys.stderr)
@@ -598,6 +644,14 @@ def main():
         del stream, into
     if args.sdpa_context:
         result["sdpa_context"] = sdpa_context(torch, w, args.steps, device)
+    if args.graph:
+        outs = [o, lse, o16] + ([dq] + dks + dvs if w.backward else [])
+        g_ms, g_match = graph_replay(torch, step, outs, args.steps)
+        result["graph"] = {"ms_per_step": round(g_ms, 4), "eager_ms_per_step": round(ms_per_step, 4),
+                           "saving_pct": round(100 * (ms_per_step - g_ms) / ms_per_step, 2),
+                           "replays_equal_eager": bool(g_match)}
+        log(f"[bench] graph replay {g_ms:.3f} ms/step (eager {ms_per_step:.3f}), "
+            f"replays equal eager: {g_match}")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w, rank, perm_np, first_np)
