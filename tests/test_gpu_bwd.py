@@ -78,6 +78,53 @@ def test_bwd_chunk_kernel_ragged(mm, d, hq, hkv):
     assert np.all(to_np(dq)[empty] == 0)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_bwd_peaked_softmax_from_gpu_forward(mm, packed):
+    """Logits about 5.7 times the 1/sqrt(d) scale (scale 0.5 at d = 128), so most
+    rows put nearly all their weight on a few keys: the forward's running max is
+    raised many times and P spans the full fp32 range in the backward.  The
+    GPU forward's LSE and bf16 output feed the GPU backward, as in training."""
+    mmsp, _ = mm
+    import torch
+    sq, sk, hq, hkv, d, scale = 257, 300, 4, 2, 128, 0.5
+    rng = np.random.default_rng(61 + packed)
+    qp, kp = _interleaved(rng, sq, sk)
+    qs = None
+    if packed:  # three samples: every query's start is the largest cut at or below it
+        cuts = np.array([0, int(qp[sq // 3]), int(qp[2 * sq // 3])])
+        qs = cuts[np.searchsorted(cuts, qp, side="right") - 1].astype(np.int32)
+    qb, qv = normal_bf16(62, (sq, hq, d))
+    kb, kv = normal_bf16(63, (sk, hkv, d))
+    vb, vv = normal_bf16(64, (sk, hkv, d))
+    gb, gv = normal_bf16(65, (sq, hq, d))
+    qd, kd, vd, gd = (to_dev_bf16(x) for x in (qb, kb, vb, gb))
+    qs_d = to_dev_i32(qs) if packed else None
+    o, lse = mmsp.attn_fwd_chunk(qd, kd, vd, to_dev_i32(qp), to_dev_i32(kp), scale=scale,
+                                 q_start=qs_d)
+    o_ref, lse_ref = oracle.attention_forward(qv, kv, vv, qp, kp, scale=scale, q_start=qs)
+    assert_close_abs(to_np(o), o_ref, what="O")
+    finite = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(to_np(lse)), finite)
+    assert np.abs(to_np(lse)[finite] - lse_ref[finite]).max() <= 2e-2
+    o16 = o.to(torch.bfloat16)
+    delta = mmsp.attn_bwd_preprocess(o16, gd)
+    dq = torch.zeros((sq, hq, d), dtype=torch.float32, device="cuda")
+    dk, dv = mmsp.attn_bwd_chunk(qd, kd, vd, gd, lse, delta, to_dev_i32(qp), to_dev_i32(kp), dq,
+                                 scale=scale, q_start=qs_d)
+    delta_ref = oracle.bwd_delta(o16.float().cpu().numpy().astype(np.float64), gv)
+    dq_ref, dk_ref, dv_ref = oracle.attention_backward(qv, kv, vv, gv, lse_ref, delta_ref, qp,
+                                                       kp, scale=scale, q_start=qs)
+    mq, mk, mv = oracle.attention_backward_magnitudes(qv, kv, vv, gv, o_ref, lse_ref, qp, kp,
+                                                      scale=scale, q_start=qs)
+    # Gradients reach ~20 at this scale (dQ, dK carry the scale), so the
+    # absolute and RMS bounds that suit unit-scale values do not apply; the
+    # elementwise bound 2u * sum|terms| scales with each element's own terms.
+    loose = dict(mean_rel=np.inf, max_abs=np.inf, mean_abs=np.inf)
+    assert_close_rms(to_np(dq), dq_ref, bound=mq, what="dQ", **loose)
+    assert_close_rms(to_np(dk), dk_ref, bound=mk, what="dK", **loose)
+    assert_close_rms(to_np(dv), dv_ref, bound=mv, what="dV", **loose)
+
+
 def test_bwd_chunk_non_causal_and_accumulate(mm):
     mmsp, _ = mm
     import torch
