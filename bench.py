@@ -160,8 +160,10 @@ def read_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(w, rank, perm_np, first_np=None):
-    """The oracle, as it stands, on a few query heads of the workload."""
+def cpu_baseline(w, rank, perm_np, first_np=None, full=False):
+    """The oracle, as it stands, on a few query heads of the workload (a
+    bounded sample), or with ``full`` on every head and row, one group of
+    heads at a time."""
     import oracle
     from threadpoolctl import threadpool_info
     t_gen = time.time()
@@ -174,11 +176,6 @@ def cpu_baseline(w, rank, perm_np, first_np=None):
     target = 4 if w.backward else 8
     nkv = max(1, min(w.hkv, round(target / g)))
     nh = nkv * g
-    q1 = np.ascontiguousarray(qv[:, :nh, :])
-    k1 = [np.ascontiguousarray(kv[c][:, :nkv, :]) for c in range(w.n_chunks)]
-    v1 = [np.ascontiguousarray(vv[c][:, :nkv, :]) for c in range(w.n_chunks)]
-    g1 = np.ascontiguousarray(gv[:, :nh, :]) if gv is not None else None
-    del qv, kv, vv, gv
     qp = rank_positions(perm_np, w, rank)
     qs_all = rank_positions(first_np, w, rank) if first_np is not None else None
     kps = [perm_np[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
@@ -189,25 +186,34 @@ def cpu_baseline(w, rank, perm_np, first_np=None):
     rows = None
     pairs_all = sum(visible_pairs_per_chunk(w, perm_np, rank, first_np))
     flops_all = per_pair * pairs_all
-    if flops_all > CPU_BASELINE_FLOP_BUDGET:
+    if flops_all > CPU_BASELINE_FLOP_BUDGET and not full:
         n_rows = max(64, int(w.shard * CPU_BASELINE_FLOP_BUDGET / flops_all))
         rows = np.sort(np.random.default_rng(0).choice(w.shard, n_rows, replace=False))
     qr = qp if rows is None else qp[rows]
     qsr = None if qs_all is None else (qs_all if rows is None else qs_all[rows])
     log(f"[bench] cpu_baseline inputs ready in {time.time() - t_gen:.1f}s")
-    t0 = time.time()
-    o, lse = oracle.ring_forward(q1, k1, v1, qp, kps, order=order, rows=rows, q_start=qs_all)
-    t_fwd = time.time() - t0
-    t_bwd = 0.0
-    if g1 is not None:
-        t1 = time.time()
-        g1r = g1 if rows is None else g1[rows]
-        q1r = q1 if rows is None else q1[rows]
-        delta = oracle.bwd_delta(o, g1r)
-        for c in order:
-            oracle.attention_backward(q1r, k1[c], v1[c], g1r, lse, delta, qr, kps[c],
-                                      q_start=qsr)
-        t_bwd = time.time() - t1
+    groups = range(0, w.hkv, nkv) if full else [0]
+    t_fwd = t_bwd = 0.0
+    for kv0 in groups:
+        h0 = kv0 * g
+        q1 = np.ascontiguousarray(qv[:, h0:h0 + nh, :])
+        k1 = [np.ascontiguousarray(kv[c][:, kv0:kv0 + nkv, :]) for c in range(w.n_chunks)]
+        v1 = [np.ascontiguousarray(vv[c][:, kv0:kv0 + nkv, :]) for c in range(w.n_chunks)]
+        g1 = np.ascontiguousarray(gv[:, h0:h0 + nh, :]) if gv is not None else None
+        t0 = time.time()
+        o, lse = oracle.ring_forward(q1, k1, v1, qp, kps, order=order, rows=rows, q_start=qs_all)
+        t_fwd += time.time() - t0
+        if g1 is not None:
+            t1 = time.time()
+            g1r = g1 if rows is None else g1[rows]
+            q1r = q1 if rows is None else q1[rows]
+            delta = oracle.bwd_delta(o, g1r)
+            for c in order:
+                oracle.attention_backward(q1r, k1[c], v1[c], g1r, lse, delta, qr, kps[c],
+                                          q_start=qsr)
+            t_bwd += time.time() - t1
+        if full:
+            log(f"[bench] cpu_baseline heads {h0}-{h0 + nh - 1}: fwd {t_fwd:.1f}s bwd {t_bwd:.1f}s")
     pairs = 0
     for c in range(w.n_chunks):
         kc = np.sort(kps[c])
@@ -215,15 +221,16 @@ def cpu_baseline(w, rank, perm_np, first_np=None):
         if qsr is not None:
             n_vis = n_vis - np.searchsorted(kc, qsr, side="left")
         pairs += int(np.maximum(n_vis, 0).sum())
-    flops = per_pair * pairs
+    flops = per_pair * pairs * len(groups)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     elapsed = t_fwd + t_bwd
+    heads = f"all {w.hq} query heads" if full else f"query heads 0-{nh - 1} of {w.hq}"
     return {
         "value": round(flops / elapsed / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"query heads 0-{nh - 1} of {w.hq}, "
+        "sample": (f"{heads}, "
                    + (f"all {w.shard} query rows" if rows is None else
                       f"{len(rows)} seeded random query rows of {w.shard}")
                    + f" ({flops / (per_pair / nh * w.hq) / pairs_all:.4f}"
@@ -335,6 +342,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--unfused", action="store_true", help="separate merge pass per chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle on the whole workload (every head and row, one group of "
+                         "heads at a time) instead of the bounded sample; minutes of CPU work")
     ap.add_argument("--rope-theta", type=float, default=None,
                     help="rotate Q and every K chunk at their global positions with this rotary "
                          "base before the ring and rotate dQ/dK back after the backward "
@@ -653,8 +663,9 @@ def main():
         log(f"[bench] graph replay {g_ms:.3f} ms/step (eager {ms_per_step:.3f}), "
             f"replays equal eager: {g_match}")
     if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host (bounded sample)")
-        result["cpu_baseline"] = cpu_baseline(w, rank, perm_np, first_np)
+        log("[bench] timing the oracle on the host ("
+            + ("whole workload" if args.cpu_full else "bounded sample") + ")")
+        result["cpu_baseline"] = cpu_baseline(w, rank, perm_np, first_np, full=args.cpu_full)
     print(json.dumps(result), flush=True)
 
 
