@@ -35,6 +35,11 @@
  *    nonzero return means nothing was launched.  Calls are thread-safe and
  *    keep no global device state.  Position arrays must be strictly
  *    increasing (a precondition, not checked).
+ *  - No entry point allocates, synchronises or enqueues a memset (buffers
+ *    that must start at zero are cleared by the library's own kernels), so
+ *    the enqueued work can be captured in a HIP graph; the host-only
+ *    queries (status strings, version, device info, workspace size) launch
+ *    nothing.
  */
 #ifndef MMSP_H
 #define MMSP_H
