@@ -104,14 +104,24 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on_current_device(t, name):
+    """The work is enqueued on the current device's stream, so every tensor
+    must live on that device."""
+    import torch
+    if t.device.type != "cuda":
+        raise TypeError(f"{name}: expected a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
 def _need(t, dtype, name, ndim=None):
     import torch
     if t is None:
         return
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
-    if t.device.type != "cuda":
-        raise TypeError(f"{name}: expected a device tensor")
+    _on_current_device(t, name)
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     if ndim is not None and t.dim() != ndim:
@@ -195,14 +205,16 @@ def shard_gather(x, rows, out=None):
     ``rows[i]`` is outside ``x``); ``rows`` int32 on the device."""
     import torch
     _need(rows, torch.int32, "rows", 1)
-    if x.device.type != "cuda" or not x.is_contiguous():
-        raise ValueError("x: expected a contiguous device tensor")
+    _on_current_device(x, "x")
+    if not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x: expected a contiguous tensor of rows")
     shape = (rows.numel(),) + tuple(x.shape[1:])
     if out is None:
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _on_current_device(out, "out")
     if out.dtype != x.dtype or tuple(out.shape) != shape or not out.is_contiguous():
         raise ValueError(f"out: expected a contiguous {x.dtype} tensor of shape {shape}")
-    row_bytes = x[0].numel() * x.element_size()
+    row_bytes = math.prod(x.shape[1:]) * x.element_size()
     _check(lib().mmsp_shard_gather(_ptr(x), x.shape[0], _ptr(rows), rows.numel(), row_bytes,
                                    _ptr(out), _stream()), "mmsp_shard_gather")
     return out
@@ -214,12 +226,13 @@ def shard_scatter(x, rows, out):
     import torch
     _need(rows, torch.int32, "rows", 1)
     for t, n in ((x, "x"), (out, "out")):
-        if t.device.type != "cuda" or not t.is_contiguous():
-            raise ValueError(f"{n}: expected a contiguous device tensor")
+        _on_current_device(t, n)
+        if not t.is_contiguous() or t.dim() < 1:
+            raise ValueError(f"{n}: expected a contiguous tensor of rows")
     if out.dtype != x.dtype or tuple(out.shape[1:]) != tuple(x.shape[1:]) or \
             rows.numel() != x.shape[0]:
         raise ValueError("x, rows and out disagree")
-    row_bytes = x[0].numel() * x.element_size()
+    row_bytes = math.prod(x.shape[1:]) * x.element_size()
     _check(lib().mmsp_shard_scatter(_ptr(x), x.shape[0], _ptr(rows), out.shape[0], row_bytes,
                                     _ptr(out), _stream()), "mmsp_shard_scatter")
     return out
