@@ -2,11 +2,13 @@
 bench.py times (GPU shard balance -> fused ring forward -> backward).
 
 The oracle cannot redo whole 8K x 64K attentions in seconds, so outputs are
-compared on sampled query rows (all heads; rows at tile, half and block
+mostly compared on sampled query rows (all heads; rows at tile, half and block
 boundaries plus seeded random rows), on whole heads for dK/dV (elementwise,
 within the bf16 rounding bound), and through an identity that holds at any
 size: the sum of dV over all keys of all chunks equals the sum of dO over the
-rows that see any key (each row's weights sum to one).
+rows that see any key (each row's weights sum to one).  The bench's forward
+configuration is also compared on every element (about a minute of oracle
+work).
 """
 
 import numpy as np
@@ -114,6 +116,19 @@ def test_forward_full_size_sampled_rows(mm, w):
     assert_close_abs(out["lse"][:, rows], l_ref, what=f"{w.name} LSE")
     # every row of a shard sees at least its own diagonal key
     assert np.isfinite(out["lse"]).all()
+
+
+def test_forward_full_size_every_element(mm):
+    """The bench's forward configuration (rank 0 of zigzag P = 8 over 65,536
+    tokens, 32 heads, d = 128, 8 chunks, fused merge) compared on every element
+    of O and LSE, not a sample: about a minute of oracle work on 16 host cores."""
+    w = RANK_FWD
+    out, host = _run(mm, w)
+    print(f"[full] {w.name}: oracle on all {w.shard} rows x {w.hq} heads", flush=True)
+    o_ref, l_ref = oracle.ring_forward(host["q"], list(host["k"]), list(host["v"]), host["qp"],
+                                       host["kps"], order=host["order"])
+    assert_close_abs(out["o"], o_ref, what=f"{w.name} O, every element")
+    assert_close_abs(out["lse"], l_ref, what=f"{w.name} LSE, every element")
 
 
 def test_training_step_full_size(mm):
