@@ -365,9 +365,20 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step into a HIP graph and time its replays (resident "
                          "chunks only); replays are checked bit for bit against the eager step")
+    ap.add_argument("--native-ring", action="store_true",
+                    help="also time the step with the ring loop in the library (mmsp_ring_forward "
+                         "/ mmsp_ring_backward) and check its outputs against the Python driver's")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
+    if (args.graph or args.native_ring) and (args.ring_copy or args.rope_theta):
+        print("--graph and --native-ring run the resident-chunk step without rotary passes; they "
+              "do not combine with --ring-copy or --rope-theta", file=sys.stderr)
+        sys.exit(2)
+    if args.native_ring and args.unfused:
+        print("--native-ring runs the fused merge; it does not combine with --unfused",
+              file=sys.stderr)
+        sys.exit(2)
     if args.graph and args.ring_copy:
         print("--graph captures the resident-chunk step; it does not combine with --ring-copy",
               file=sys.stderr)
@@ -438,7 +449,8 @@ def main():
     dk_sent = [torch.empty_like(t) for t in dks] if (rx is not None and w.backward) else None
     dv_sent = [torch.empty_like(t) for t in dvs] if (rx is not None and w.backward) else None
 
-    def step(received=args.ring_copy):
+    def balance():
+        """Shard balance on the GPU: (perm, token sample starts or None, this rank's starts)."""
         first = qs = None
         if w.layout == "packed":  # every packed sample zigzagged on its own
             perm, _, first = mmsp.shard_balance_packed(starts, n, w.n_ranks)
@@ -449,6 +461,10 @@ def main():
             perm, _ = mmsp.shard_balance(n, w.n_ranks, mode, w.granularity,
                                          labels=labels if mode == mmsp.BALANCE_MODALITY else None,
                                          with_inverse=False)
+        return perm, first, qs
+
+    def step(received=args.ring_copy):
+        perm, first, qs = balance()
         qp = perm[rank * w.shard:(rank + 1) * w.shard]
         kps = [perm[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
         qq, kk = rope_in(qp, kps) if theta else (q, ks)
@@ -654,6 +670,43 @@ def main():
         del stream, into
     if args.sdpa_context:
         result["sdpa_context"] = sdpa_context(torch, w, args.steps, device)
+    if args.native_ring:
+        outs = [o, lse, o16] + ([dq] + dks + dvs if w.backward else [])
+
+        def native_step():
+            perm_n, _, qs_n = balance()
+            qp_n = perm_n[rank * w.shard:(rank + 1) * w.shard]
+            kps_n = [perm_n[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
+            mmsp.ring_forward_native(q, ks, vs, qp_n, kps_n, rank=rank, o=o, lse=lse,
+                                     o_final=o16, q_start=qs_n)
+            if w.backward:
+                mmsp.ring_backward_native(q, ks, vs, dout, o16, lse, qp_n, kps_n, rank=rank,
+                                          dq=dq, dks=dks, dvs=dvs, delta=delta, q_start=qs_n)
+
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        want = [t.clone() for t in outs]
+        for t in outs:
+            t.zero_()
+        native_step()
+        torch.cuda.synchronize()
+        n_match = all(torch.equal(a, b) for a, b in zip(outs, want))
+        for _ in range(args.warmup):
+            native_step()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(args.steps):
+            native_step()
+        ev[1].record()
+        torch.cuda.synchronize()
+        n_ms = ev[0].elapsed_time(ev[1]) / args.steps
+        result["native_ring"] = {"ms_per_step": round(n_ms, 4),
+                                 "python_driver_ms_per_step": round(ms_per_step, 4),
+                                 "outputs_equal_python_driver": bool(n_match)}
+        log(f"[bench] native ring {n_ms:.3f} ms/step (Python driver {ms_per_step:.3f}), "
+            f"outputs equal: {n_match}")
     if args.graph:
         outs = [o, lse, o16] + ([dq] + dks + dvs if w.backward else [])
         g_ms, g_match = graph_replay(torch, step, outs, args.steps)

@@ -274,6 +274,52 @@ int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, cons
                                uint32_t flags, float* dq_acc, float* dk, float* dv,
                                void* stream);
 
+/* ---- a4: one rank's ring loop over resident chunks -----------------------
+ * "LongVILA Guide ...", section "Implementation: PyTorch Distributed
+ * Pipeline and Token Routing": at ring step t a rank computes attention of
+ * its local queries against the chunk it holds, which came from rank
+ * (rank - t) mod P; section "Multi-Modal Sequence Parallelism (MM-SP)
+ * Mechanics", item 3: one kernel per step.  With all n_chunks chunks resident,
+ * these calls visit chunk (rank - t) mod n_chunks at step t and make the same
+ * launches, in the same order, as calling the chunk entry points one by one.
+ *
+ * k_chunks, v_chunks (bf16 [sk][hkv][d]), k_pos_chunks (int32 [sk]), and for
+ * the backward dk_chunks, dv_chunks (fp32 [sk][hkv][d]): HOST arrays of
+ * n_chunks DEVICE pointers, read during the call only.  Every chunk has sk
+ * keys.  q, q_pos, q_start, scale and the shapes are as in
+ * mmsp_attn_fwd_chunk(_packed); q_start (nullable) selects packed samples
+ * and needs MMSP_CAUSAL.  0 <= rank < n_chunks.
+ *
+ * mmsp_ring_forward: the first step writes (o fp32 [sq][hq][d], lse fp32
+ *   [hq][sq]), later steps merge into them (MMSP_ACCUMULATE); then, if
+ *   o_final_bf16 is not NULL, the bf16 output [sq][hq][d] is written as
+ *   mmsp_lse_merge does.  flags: MMSP_CAUSAL or 0.
+ * mmsp_ring_backward: delta (fp32 [hq][sq]) from o_bf16 and dout with dq
+ *   (fp32 [sq][hq][d]) zeroed, as mmsp_attn_bwd_preprocess; then one backward
+ *   per chunk in ring order: dq accumulates every chunk's contribution and
+ *   dk_chunks[c], dv_chunks[c] are overwritten (added to with
+ *   MMSP_ACCUMULATE).  lse is the final LSE of the forward.  flags:
+ *   MMSP_CAUSAL and/or MMSP_ACCUMULATE.
+ *
+ * Errors: every argument of every chunk is checked before the first launch
+ * (NULL array or entry: MMSP_ERR_NULL; n_chunks <= 0 or rank out of range:
+ * MMSP_ERR_SHAPE; other codes as the chunk entry points).  MMSP_ERR_HIP from
+ * a launch part-way returns at once and leaves the earlier launches
+ * enqueued.
+ */
+int mmsp_ring_forward(const void* q, const void* const* k_chunks, const void* const* v_chunks,
+                      const int32_t* q_pos, const int32_t* const* k_pos_chunks,
+                      const int32_t* q_start, int32_t n_chunks, int32_t rank, int32_t sq,
+                      int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
+                      uint32_t flags, float* o, float* lse, void* o_final_bf16, void* stream);
+int mmsp_ring_backward(const void* q, const void* const* k_chunks, const void* const* v_chunks,
+                       const void* dout, const void* o_bf16, const float* lse,
+                       const int32_t* q_pos, const int32_t* const* k_pos_chunks,
+                       const int32_t* q_start, int32_t n_chunks, int32_t rank, int32_t sq,
+                       int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
+                       uint32_t flags, float* delta, float* dq, float* const* dk_chunks,
+                       float* const* dv_chunks, void* stream);
+
 /* ---- rotary position embedding at global positions ------------------------
  * "LongVILA Guide ...", section "Three-Stage Long-Context Alignment
  * Curriculum", stage 2: the rotary base theta is raised to 10,000,000 for the

@@ -284,6 +284,71 @@ int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, cons
                   flags, dq_acc, dk, dv, stream);
 }
 
+// One rank's ring loop: chunk (rank - t) mod n_chunks at step t.  Every
+// argument of every chunk is checked before the first launch.
+int mmsp_ring_forward(const void* q, const void* const* k_chunks, const void* const* v_chunks,
+                      const int32_t* q_pos, const int32_t* const* k_pos_chunks,
+                      const int32_t* q_start, int32_t n_chunks, int32_t rank, int32_t sq,
+                      int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
+                      uint32_t flags, float* o, float* lse, void* o_final_bf16, void* stream) {
+  if ((flags & ~(uint32_t)MMSP_CAUSAL) != 0) return MMSP_ERR_UNSUPPORTED;
+  const bool causal = (flags & MMSP_CAUSAL) != 0;
+  if (q_start && !causal) return MMSP_ERR_UNSUPPORTED;
+  if (!k_chunks || !v_chunks || (causal && !k_pos_chunks)) return MMSP_ERR_NULL;
+  if (n_chunks <= 0 || rank < 0 || rank >= n_chunks) return MMSP_ERR_SHAPE;
+  if (!q || !o || !lse || (causal && !q_pos)) return MMSP_ERR_NULL;
+  for (int c = 0; c < n_chunks; ++c)
+    if (!k_chunks[c] || !v_chunks[c] || (causal && !k_pos_chunks[c])) return MMSP_ERR_NULL;
+  int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
+  if (st != MMSP_OK) return st;
+  for (int t = 0; t < n_chunks; ++t) {
+    const int c = ((rank - t) % n_chunks + n_chunks) % n_chunks;
+    const uint32_t f = flags | (t > 0 ? (uint32_t)MMSP_ACCUMULATE : 0u);
+    st = attn_fwd(q, k_chunks[c], v_chunks[c], q_pos, q_start, causal ? k_pos_chunks[c] : nullptr,
+                  sq, sk, hq, hkv, d, scale, f, o, lse, stream);
+    if (st != MMSP_OK) return st;
+  }
+  if (o_final_bf16 == nullptr) return MMSP_OK;
+  return check_hip(mmsp::launch_lse_merge(o, lse, nullptr, nullptr, sq, hq, d,
+                                          static_cast<uint16_t*>(o_final_bf16),
+                                          as_stream(stream)));
+}
+
+int mmsp_ring_backward(const void* q, const void* const* k_chunks, const void* const* v_chunks,
+                       const void* dout, const void* o_bf16, const float* lse,
+                       const int32_t* q_pos, const int32_t* const* k_pos_chunks,
+                       const int32_t* q_start, int32_t n_chunks, int32_t rank, int32_t sq,
+                       int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
+                       uint32_t flags, float* delta, float* dq, float* const* dk_chunks,
+                       float* const* dv_chunks, void* stream) {
+  if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
+  const bool causal = (flags & MMSP_CAUSAL) != 0;
+  if (q_start && !causal) return MMSP_ERR_UNSUPPORTED;
+  if (!k_chunks || !v_chunks || !dk_chunks || !dv_chunks || (causal && !k_pos_chunks))
+    return MMSP_ERR_NULL;
+  if (n_chunks <= 0 || rank < 0 || rank >= n_chunks) return MMSP_ERR_SHAPE;
+  if (!q || !dout || !o_bf16 || !lse || !delta || !dq || (causal && !q_pos)) return MMSP_ERR_NULL;
+  for (int c = 0; c < n_chunks; ++c)
+    if (!k_chunks[c] || !v_chunks[c] || !dk_chunks[c] || !dv_chunks[c] ||
+        (causal && !k_pos_chunks[c]))
+      return MMSP_ERR_NULL;
+  int st = check_attn_shapes(sq, sk, hq, hkv, d, scale);
+  if (st != MMSP_OK) return st;
+  // delta from the bf16 output; dq zeroed in the same pass
+  st = check_hip(mmsp::launch_bwd_preprocess(static_cast<const uint16_t*>(o_bf16),
+                                             static_cast<const uint16_t*>(dout), sq, hq, d, delta,
+                                             dq, as_stream(stream)));
+  if (st != MMSP_OK) return st;
+  for (int t = 0; t < n_chunks; ++t) {
+    const int c = ((rank - t) % n_chunks + n_chunks) % n_chunks;
+    st = attn_bwd(q, k_chunks[c], v_chunks[c], dout, lse, delta, q_pos, q_start,
+                  causal ? k_pos_chunks[c] : nullptr, sq, sk, hq, hkv, d, scale, flags, dq,
+                  dk_chunks[c], dv_chunks[c], stream);
+    if (st != MMSP_OK) return st;
+  }
+  return MMSP_OK;
+}
+
 int mmsp_rope(const void* x, void* y, int32_t dtype, const int32_t* pos, int32_t s, int32_t h,
               int32_t d, double theta, int32_t inverse, void* stream) {
   if (!x || !y || !pos) return MMSP_ERR_NULL;

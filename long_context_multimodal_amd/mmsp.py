@@ -52,6 +52,11 @@ SIGNATURES = {
     "mmsp_attn_bwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                   _I32, _I32, _I32, _I32, _I32, _F32, _U32, _VP,
                                                   _VP, _VP, _VP]),
+    "mmsp_ring_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
+                                         _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
+    "mmsp_ring_backward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
+                                          _I32, _I32, _I32, _I32, _I32, _F32, _U32, _VP, _VP,
+                                          _VP, _VP, _VP]),
 }
 
 _lib = None
@@ -403,6 +408,128 @@ def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=
                                      float(scale), flags, _ptr(dq_acc), _ptr(dk), _ptr(dv),
                                      _stream()), "mmsp_attn_bwd_chunk")
     return dk, dv
+
+
+# ---------------------------------------------------------------- a4 in the library
+def _pointer_array(tensors):
+    """Host array of the tensors' device pointers (kept alive by the caller)."""
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def _ring_chunks(q, k_chunks, v_chunks, q_pos, k_pos_chunks, q_start, causal):
+    """Check a ring's tensors; return (sq, hq, d, sk, hkv)."""
+    import torch
+    n = len(k_chunks)
+    if n == 0 or len(v_chunks) != n or (causal and len(k_pos_chunks) != n):
+        raise ValueError("one K, V (and, with the causal mask, position array) per chunk")
+    _need(q, torch.bfloat16, "q", 3)
+    sq, hq, d = q.shape
+    _need(k_chunks[0], torch.bfloat16, "k[0]", 3)
+    sk, hkv = k_chunks[0].shape[0], k_chunks[0].shape[1]
+    for c in range(n):
+        _need(k_chunks[c], torch.bfloat16, f"k[{c}]", 3)
+        _need(v_chunks[c], torch.bfloat16, f"v[{c}]", 3)
+        _shape(k_chunks[c], (sk, hkv, d), f"k[{c}]")
+        _shape(v_chunks[c], (sk, hkv, d), f"v[{c}]")
+        if causal:
+            _need(k_pos_chunks[c], torch.int32, f"k_pos[{c}]", 1)
+            _shape(k_pos_chunks[c], (sk,), f"k_pos[{c}]")
+    if causal:
+        _need(q_pos, torch.int32, "q_pos", 1)
+        _shape(q_pos, (sq,), "q_pos")
+    if q_start is not None:
+        if not causal:
+            raise ValueError("q_start needs the causal mask")
+        _need(q_start, torch.int32, "q_start", 1)
+        _shape(q_start, (sq,), "q_start")
+    if CHECK_POSITIONS and causal:
+        for c in range(n):
+            _debug_check(q_pos, k_pos_chunks[c], q_start)
+    return sq, hq, d, sk, hkv
+
+
+def ring_forward_native(q, k_chunks, v_chunks, q_pos, k_pos_chunks, rank=0, scale=None,
+                        causal=True, o=None, lse=None, o_final=None, q_start=None):
+    """The whole ring forward in one library call (``mmsp_ring_forward``):
+    chunk ``(rank - t) mod P`` at step ``t``, fused merge, bf16 output.
+    Returns ``(o fp32, lse fp32, o_final bf16)`` like ``ring.ring_forward``."""
+    import torch
+    sq, hq, d, sk, hkv = _ring_chunks(q, k_chunks, v_chunks, q_pos, k_pos_chunks, q_start,
+                                      causal)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((sq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, sq), dtype=torch.float32, device=q.device)
+    if o_final is None:
+        o_final = torch.empty((sq, hq, d), dtype=torch.bfloat16, device=q.device)
+    _need(o, torch.float32, "o", 3)
+    _need(lse, torch.float32, "lse", 2)
+    _need(o_final, torch.bfloat16, "o_final", 3)
+    _shape(o, (sq, hq, d), "o")
+    _shape(lse, (hq, sq), "lse")
+    _shape(o_final, (sq, hq, d), "o_final")
+    ks, vs = _pointer_array(k_chunks), _pointer_array(v_chunks)
+    kps = _pointer_array(k_pos_chunks) if causal else None
+    _check(lib().mmsp_ring_forward(_ptr(q), ctypes.cast(ks, _VP), ctypes.cast(vs, _VP),
+                                   _ptr(q_pos if causal else None),
+                                   ctypes.cast(kps, _VP) if kps is not None else None,
+                                   _ptr(q_start), len(k_chunks), rank, sq, sk, hq, hkv, d,
+                                   float(scale), CAUSAL if causal else 0, _ptr(o), _ptr(lse),
+                                   _ptr(o_final), _stream()), "mmsp_ring_forward")
+    return o, lse, o_final
+
+
+def ring_backward_native(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks, rank=0,
+                         scale=None, causal=True, dq=None, dks=None, dvs=None, delta=None,
+                         q_start=None, accumulate=False):
+    """The whole ring backward in one library call (``mmsp_ring_backward``):
+    delta and zeroed dq, then every chunk in ring order.  Returns
+    ``(dq, [dk_c], [dv_c])`` like ``ring.ring_backward``."""
+    import torch
+    sq, hq, d, sk, hkv = _ring_chunks(q, k_chunks, v_chunks, q_pos, k_pos_chunks, q_start,
+                                      causal)
+    n = len(k_chunks)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _need(dout, torch.bfloat16, "dout", 3)
+    _need(o_bf16, torch.bfloat16, "o_bf16", 3)
+    _need(lse, torch.float32, "lse", 2)
+    _shape(dout, (sq, hq, d), "dout")
+    _shape(o_bf16, (sq, hq, d), "o_bf16")
+    _shape(lse, (hq, sq), "lse")
+    if dq is None:
+        dq = torch.empty((sq, hq, d), dtype=torch.float32, device=q.device)
+    if delta is None:
+        delta = torch.empty((hq, sq), dtype=torch.float32, device=q.device)
+    if dks is None:
+        dks = [torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device) for _ in range(n)]
+    if dvs is None:
+        dvs = [torch.empty((sk, hkv, d), dtype=torch.float32, device=q.device) for _ in range(n)]
+    _need(dq, torch.float32, "dq", 3)
+    _need(delta, torch.float32, "delta", 2)
+    _shape(dq, (sq, hq, d), "dq")
+    _shape(delta, (hq, sq), "delta")
+    if len(dks) != n or len(dvs) != n:
+        raise ValueError("one dK and one dV per chunk")
+    for c in range(n):
+        _need(dks[c], torch.float32, f"dk[{c}]", 3)
+        _need(dvs[c], torch.float32, f"dv[{c}]", 3)
+        _shape(dks[c], (sk, hkv, d), f"dk[{c}]")
+        _shape(dvs[c], (sk, hkv, d), f"dv[{c}]")
+    ks, vs = _pointer_array(k_chunks), _pointer_array(v_chunks)
+    kps = _pointer_array(k_pos_chunks) if causal else None
+    dka, dva = _pointer_array(dks), _pointer_array(dvs)
+    flags = (CAUSAL if causal else 0) | (ACCUMULATE if accumulate else 0)
+    _check(lib().mmsp_ring_backward(_ptr(q), ctypes.cast(ks, _VP), ctypes.cast(vs, _VP),
+                                    _ptr(dout), _ptr(o_bf16), _ptr(lse),
+                                    _ptr(q_pos if causal else None),
+                                    ctypes.cast(kps, _VP) if kps is not None else None,
+                                    _ptr(q_start), n, rank, sq, sk, hq, hkv, d, float(scale),
+                                    flags, _ptr(delta), _ptr(dq), ctypes.cast(dka, _VP),
+                                    ctypes.cast(dva, _VP), _stream()), "mmsp_ring_backward")
+    return dq, dks, dvs
 
 
 # ---------------------------------------------------------------- rotary embedding

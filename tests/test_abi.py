@@ -210,3 +210,66 @@ def test_check_positions_rejects():
     assert f(None, None, 16, FAKE, None) == -1
     assert f(FAKE, None, 16, None, None) == -1
     assert f(FAKE, None, 0, FAKE, None) == -2
+
+
+def _arr(n, none_at=None):
+    a = (ctypes.c_void_p * n)(*([0x1000] * n))
+    if none_at is not None:
+        a[none_at] = None
+    return ctypes.cast(a, ctypes.c_void_p), a
+
+
+def ring_fwd(**kw):
+    n = kw.pop("n", 4)
+    ks, ka = _arr(n, kw.pop("k_none_at", None))
+    vs, va = _arr(n)
+    kps, kpa = _arr(n)
+    a = dict(q=FAKE, ks=ks, vs=vs, qp=FAKE, kps=kps, qs=None, n=n, rank=1, sq=128, sk=128, hq=4,
+             hkv=2, d=128, scale=0.088, flags=1, o=FAKE, lse=FAKE, of=None)
+    a.update(kw)
+    return mmsp.lib().mmsp_ring_forward(a["q"], a["ks"], a["vs"], a["qp"], a["kps"], a["qs"],
+                                        a["n"], a["rank"], a["sq"], a["sk"], a["hq"], a["hkv"],
+                                        a["d"], a["scale"], a["flags"], a["o"], a["lse"], a["of"],
+                                        None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=None), -1), (dict(kps=None), -1), (dict(k_none_at=2), -1), (dict(q=None), -1),
+    (dict(qp=None), -1), (dict(lse=None), -1),
+    (dict(n=0), -2), (dict(rank=4), -2), (dict(rank=-1), -2), (dict(sq=0), -2),
+    (dict(scale=0.0), -2),
+    (dict(flags=2), -3), (dict(flags=0, qs=FAKE), -3), (dict(d=96), -3),
+    (dict(hq=6, hkv=4), -4),
+])
+def test_ring_forward_rejects(kw, code):
+    """Every argument of every chunk is checked before the first launch."""
+    assert ring_fwd(**kw) == code
+
+
+def ring_bwd(**kw):
+    n = kw.pop("n", 4)
+    ks, ka = _arr(n)
+    vs, va = _arr(n)
+    kps, kpa = _arr(n)
+    dks, dka = _arr(n)
+    dvs, dva = _arr(n, kw.pop("dv_none_at", None))
+    a = dict(q=FAKE, ks=ks, vs=vs, do=FAKE, o16=FAKE, lse=FAKE, qp=FAKE, kps=kps, qs=None, n=n,
+             rank=0, sq=128, sk=128, hq=4, hkv=2, d=128, scale=0.088, flags=1, delta=FAKE,
+             dq=FAKE, dks=dks, dvs=dvs)
+    a.update(kw)
+    return mmsp.lib().mmsp_ring_backward(a["q"], a["ks"], a["vs"], a["do"], a["o16"], a["lse"],
+                                         a["qp"], a["kps"], a["qs"], a["n"], a["rank"], a["sq"],
+                                         a["sk"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                         a["flags"], a["delta"], a["dq"], a["dks"], a["dvs"],
+                                         None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dks=None), -1), (dict(dv_none_at=3), -1), (dict(do=None), -1), (dict(o16=None), -1),
+    (dict(delta=None), -1), (dict(dq=None), -1),
+    (dict(n=0), -2), (dict(rank=7), -2), (dict(sk=0), -2),
+    (dict(flags=16), -3), (dict(flags=2, qs=FAKE), -3), (dict(d=32), -3),
+    (dict(hq=5, hkv=2), -4),
+])
+def test_ring_backward_rejects(kw, code):
+    assert ring_bwd(**kw) == code
