@@ -1,4 +1,5 @@
-"""Build ``libmmsp.so`` (all HIP sources of ``csrc/``) for gfx950 with hipcc.
+"""Build ``libmmsp.so`` (all HIP sources of ``csrc/``) for gfx950 with hipcc,
+and ``mmsp_ring_step``, a native program that calls only its C-ABI.
 
 Usage: ``python -m long_context_multimodal_amd.build`` (or ``build()``).  The
 library lands next to this file; objects go to ``_build/`` at the repo root.
@@ -16,6 +17,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmmsp.so")
+# a native caller of the C-ABI (no Python): one rank's training step from a file
+TOOL_SRC = os.path.join(PKG, "ring_step.cpp")
+TOOL = os.path.join(PKG, "mmsp_ring_step")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -65,6 +69,12 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, OUT)
+    tmp = TOOL + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, TOOL_SRC, "-L", PKG, "-lmmsp", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building {os.path.basename(TOOL)} failed:\n{r.stderr}")
+    os.replace(tmp, TOOL)
     return OUT
 
 

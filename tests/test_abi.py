@@ -273,3 +273,18 @@ def ring_bwd(**kw):
 ])
 def test_ring_backward_rejects(kw, code):
     assert ring_bwd(**kw) == code
+
+
+def test_native_program_rejects_bad_input(tmp_path):
+    """The native C-ABI caller checks its input file before touching the GPU."""
+    import subprocess
+    from long_context_multimodal_amd.build import TOOL
+    if not os.path.exists(TOOL):
+        pytest.skip("mmsp_ring_step not built")
+    bad = tmp_path / "bad.bin"
+    bad.write_bytes(b"\0" * 32)
+    r = subprocess.run([TOOL, str(bad), str(tmp_path / "out.bin")], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 1 and "bad header" in r.stderr
+    r = subprocess.run([TOOL], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
