@@ -220,3 +220,38 @@ def test_bwd_halves_equal_the_whole(mm, packed):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     assert torch.equal(dq_a, dq_b) and torch.equal(dk_a, dk_b) and torch.equal(dv_a, dv_b)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_backward_is_deterministic(mm, packed):
+    """No atomics: every dQ, dK and dV element is summed by one thread in a
+    fixed order, so two runs on the same inputs agree bit for bit."""
+    import torch
+    mmsp, ring = mm
+    n, p, rank, hq, hkv, d = 4096, 4, 2, 8, 2, 128
+    shard = n // p
+    if packed:
+        starts = torch.tensor([0, 1024, 1536, n], dtype=torch.int32, device="cuda")
+        perm, _, first = mmsp.shard_balance_packed(starts, n, p)
+        qs = first[rank * shard:(rank + 1) * shard]
+    else:
+        perm, _ = mmsp.shard_balance(n, p, with_inverse=False)
+        qs = None
+    qp = perm[rank * shard:(rank + 1) * shard]
+    kps = [perm[c * shard:(c + 1) * shard] for c in range(p)]
+    qb, _ = normal_bf16(81, (shard, hq, d))
+    kb, _ = normal_bf16(82, (p, shard, hkv, d))
+    vb, _ = normal_bf16(83, (p, shard, hkv, d))
+    gb, _ = normal_bf16(84, (shard, hq, d))
+    q, do = to_dev_bf16(qb), to_dev_bf16(gb)
+    ks = [to_dev_bf16(kb[c]) for c in range(p)]
+    vs = [to_dev_bf16(vb[c]) for c in range(p)]
+    _, lse, o16 = ring.ring_forward(q, ks, vs, qp, kps, rank=rank, q_start=qs)
+    runs = []
+    for _ in range(2):
+        dq, dks, dvs = ring.ring_backward(q, ks, vs, do, o16, lse, qp, kps, rank=rank,
+                                          q_start=qs)
+        torch.cuda.synchronize()
+        runs.append([dq.clone()] + [t.clone() for t in dks] + [t.clone() for t in dvs])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
