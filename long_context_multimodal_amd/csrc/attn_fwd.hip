@@ -25,7 +25,12 @@
 //  * online softmax in the log2 domain; the running max is only raised when
 //    a tile's max exceeds it by more than 8 (2^8 headroom in fp32/bf16), so
 //    the O rescale is skipped on most tiles without changing the result;
-//    row sums stay in fp32 (exact LSE for the merge and the backward);
+//    on unmasked tiles of rows that already have a running max the tile max
+//    is not even computed: weights are taken against the running max, and a
+//    lane row sum above 2^16 (a row max more than 16 above it) sends the
+//    tile back through the max-and-rescale path, its scores recomputed from
+//    the K tile still in LDS; row sums stay in fp32 (exact LSE for the
+//    merge and the backward);
 //  * causal tile skipping from the sorted positions: a binary search bounds
 //    the key range of the workgroup, each wave skips tiles it cannot see and
 //    masks only the tiles that straddle its rows' positions (or the tail),
@@ -248,69 +253,29 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     // each K operand's LDS read four MFMAs ahead of its use (four reads, then
     // one after every MFMA).  Without them the first half's reads sat right
     // before their MFMAs, each waiting out the LDS latency.
+    auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+      for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        const bf16x8 a = lds_read_b128(kt, kb * 32 * D * 2 + koff[ks]);
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          const bf16x8 a = lds_read_b128(kt, kb * 32 * D * 2 + koff[ks]);
 #pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb)
-          s[qb][kb] = mfma32x32x16(a, qf[qb][ks], ks == 0 ? f32x16{} : s[qb][kb]);
+          for (int qb = 0; qb < C::QB; ++qb)
+            s[qb][kb] = mfma32x32x16(a, qf[qb][ks], ks == 0 ? f32x16{} : s[qb][kb]);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < C::KS * C::NKB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < C::KS * C::NKB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    };
+    scores();
 
     uint32_t pk[C::QB][C::NKB][8];
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      // straddles this block's positions or sample starts
-      if (tail || (causal && klast > bmin[qb]) || kfirst < bqs_max[qb]) {
-        asm volatile("" ::: "memory");
-        // visible iff lo <= k_pos <= hi: one unsigned compare of k_pos - lo
-        // against hi - lo (lo = the row's sample start, INT_MIN unless
-        // packed; hi = its position, INT_MAX without the causal mask)
-        const uint32_t lo = (uint32_t)qs[qb];
-        const uint32_t span = (uint32_t)(causal ? qpos[qb] : INT_MAX) - lo;
-        if (tail) {  // key slots past the chunk read position 0: drop them too
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-              const bool hide = ((uint32_t)kp[key] - lo > span) | (key >= valid);
-              s[qb][kb][i] = hide ? -INFINITY : s[qb][kb][i];
-            }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-              s[qb][kb][i] = ((uint32_t)kp[key] - lo > span) ? -INFINITY : s[qb][kb][i];
-            }
-        }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[qb][kb][i]);
-      mt = max_halves(mt) * c;
-      if (__ballot(mt > m_run[qb] + 8.0f)) {
-        asm volatile("" ::: "memory");
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[qb] - m_new);
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) oacc[qb][mb] *= alpha;
-        l_run[qb] *= alpha;
-        m_run[qb] = m_new;
-      }
-      const float neg_m = (m_run[qb] == -INFINITY) ? 0.f : -m_run[qb];
-      float ps0 = 0.f, ps1 = 0.f;
+    auto exps = [&](int qb, float neg_m, float& ps0, float& ps1) __attribute__((always_inline)) {
+      ps0 = 0.f;
+      ps1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -320,6 +285,69 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
           pk[qb][kb][i >> 1] = pack_bf16x2(e0, e1);
           if (i & 2) ps1 += e0 + e1; else ps0 += e0 + e1;
         }
+    };
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      // straddles this block's positions or sample starts
+      const bool straddle = tail || (causal && klast > bmin[qb]) || kfirst < bqs_max[qb];
+      // Unmasked tile of rows that all have a running max: exponentiate against
+      // it directly.  A weight above 2^16 (a row max more than 16 above the
+      // running one) sends the tile down the path that finds the tile max
+      // and rescales, after recomputing the scores the exponentials used up.
+      bool slow = straddle || __ballot(m_run[qb] == -INFINITY) != 0;
+      float ps0 = 0.f, ps1 = 0.f;
+      if (!slow) {
+        exps(qb, -m_run[qb], ps0, ps1);
+        if (__ballot(!(ps0 + ps1 <= 65536.0f))) {
+          asm volatile("" ::: "memory");
+          slow = true;
+          scores();
+        }
+      }
+      if (slow) {
+        asm volatile("" ::: "memory");
+        if (straddle) {
+          // visible iff lo <= k_pos <= hi: one unsigned compare of k_pos - lo
+          // against hi - lo (lo = the row's sample start, INT_MIN unless
+          // packed; hi = its position, INT_MAX without the causal mask)
+          const uint32_t lo = (uint32_t)qs[qb];
+          const uint32_t span = (uint32_t)(causal ? qpos[qb] : INT_MAX) - lo;
+          if (tail) {  // key slots past the chunk read position 0: drop them too
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+                const bool hide = ((uint32_t)kp[key] - lo > span) | (key >= valid);
+                s[qb][kb][i] = hide ? -INFINITY : s[qb][kb][i];
+              }
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+                s[qb][kb][i] = ((uint32_t)kp[key] - lo > span) ? -INFINITY : s[qb][kb][i];
+              }
+          }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[qb][kb][i]);
+        mt = max_halves(mt) * c;
+        if (__ballot(mt > m_run[qb] + 8.0f)) {
+          asm volatile("" ::: "memory");
+          const float m_new = fmaxf(m_run[qb], mt);
+          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[qb] - m_new);
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) oacc[qb][mb] *= alpha;
+          l_run[qb] *= alpha;
+          m_run[qb] = m_new;
+        }
+        exps(qb, (m_run[qb] == -INFINITY) ? 0.f : -m_run[qb], ps0, ps1);
+      }
       l_run[qb] += ps0 + ps1;
     }
 

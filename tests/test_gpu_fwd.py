@@ -91,6 +91,39 @@ def test_chunk_peaked_softmax(mm):
     assert_close_abs(lse, l_ref, what="LSE")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("jump", [0.8, 2.0])
+def test_chunk_late_large_score(mm, causal, jump):
+    """One key of a late, unmasked tile scores far above everything before it:
+    the row max grows by about 10 (jump 0.8: weights up to 2^10 are kept
+    against the running max) or about 30 (jump 2.0: the tile is sent back
+    through the max-and-rescale path with its scores recomputed) in log2
+    units.  Both must match the oracle."""
+    sq, sk, h, d = 300, 256, 2, 128  # 4 key tiles, no tail; every tile unmasked
+    rng = np.random.default_rng(17)
+    u = rng.standard_normal(d).astype(np.float32)
+    q = u[None, None, :] + 0.1 * rng.standard_normal((sq, h, d)).astype(np.float32)
+    qb, qv = bf16_round(q)
+    kb, kv = normal_bf16(18, (sk, h, d))
+    vb, vv = normal_bf16(19, (sk, h, d))
+    big_b, big_v = bf16_round(np.float32(jump) * np.broadcast_to(u, (h, d)))
+    kb, kv = kb.copy(), kv.copy()
+    kb[200], kv[200] = big_b, big_v
+    kp = np.arange(sk, dtype=np.int32)
+    qp = np.full(sq, 10 ** 6, dtype=np.int32)  # every key visible
+    o, lse = _run_chunk(mm, qb, kb, vb, qp, kp, causal=causal)
+    o_ref, l_ref = oracle.attention_forward(qv, kv, vv, qp if causal else np.full(sq, 10 ** 6),
+                                            kp)
+    assert_close_abs(o, o_ref, what="O")
+    assert_close_abs(lse, l_ref, what="LSE")
+    # precondition of the case: in log2 units, key 200's score exceeds every
+    # row's first-tile maximum by more than 8 (jump 0.8) or 16 (jump 2.0)
+    sc = np.einsum("shd,khd->shk", qv.astype(np.float64), kv.astype(np.float64))
+    sc *= math.log2(math.e) / math.sqrt(d)
+    grow = sc[:, :, 200] - sc[:, :, :64].max(axis=-1)
+    assert grow.min() > (8 if jump < 1 else 16) and (jump > 1 or grow.max() < 16)
+
+
 def test_chunk_first_query_returns_its_value_row(mm):
     # the query at position 0 sees one key: its output is that key's V row
     sq, sk, d = 64, 64, 128
