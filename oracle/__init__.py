@@ -41,7 +41,8 @@ Modules:
 
 from .attention import attention_forward, visible_pairs  # noqa: F401
 from .merge import lse_merge, ring_forward  # noqa: F401
-from .backward import attention_backward, attention_backward_magnitudes, bwd_delta  # noqa: F401
+from .backward import (attention_abs_dp, attention_backward,  # noqa: F401
+                       attention_backward_magnitudes, bwd_delta)
 from .rope import rope, rope_angles, rope_bf16  # noqa: F401
 from .balance import (  # noqa: F401
     zigzag_perm,
