@@ -7,11 +7,17 @@ import numpy as np
 O_MAX, O_MEAN = 2e-2, 2e-3
 # gradients: the absolute bounds above; the mean error divided by the oracle
 # tensor's RMS; and, where the sums of absolute terms are supplied, the
-# elementwise rounding bound.  P and dS are rounded to bf16 (unit roundoff
-# u = 2^-9) before the gradient contractions and delta comes from the bf16 O,
-# so each element errs by at most about u * (sum of |terms|); the check allows
-# twice that.
-BF16_U = 2.0 ** -9
+# elementwise rounding bound.  The backward rounds P and dS to bf16 (8
+# significant bits, unit roundoff u = 2^-8) before the gradient contractions
+# and takes delta from the bf16 rounding of its forward's O (whose weights
+# were rounded to bf16 too), so to first order each element errs by at most
+# u * (sum of |terms|) with the sums of oracle.attention_backward_magnitudes.
+# The extra 1/8 covers what the first-order bound leaves out: second-order
+# terms (about 3u = 1.2%), fp32 accumulation (at most 2^-24 of the sum of
+# |terms| per accumulation step, a few thousand steps: about 6% of u), and the
+# fp32 exponentials and LSE (about 1e-6 relative).
+BF16_U = 2.0 ** -8
+ROUNDING_SLACK = 1.0 + 1.0 / 8
 G_MEAN = 2e-3
 
 
@@ -66,7 +72,37 @@ def assert_close_rms(got, want, bound=None, mean_rel=G_MEAN, max_abs=O_MAX, mean
     assert rel.mean() <= mean_rel, msg
     if bound is not None:
         bound = np.asarray(bound, dtype=np.float64)
-        lim = 2 * BF16_U * bound + 1e-6 * np.abs(want).max()
+        lim = ROUNDING_SLACK * BF16_U * bound + 1e-6 * np.abs(want).max()
         worst = float((err / lim).max())
-        assert worst <= 1.0, f"{msg}; exceeds 2u*sum|terms| by x{worst:.2f}"
+        assert worst <= 1.0, f"{msg}; exceeds (1+1/8) u sum|terms| by x{worst:.2f}"
     return float(rel.max()), float(rel.mean())
+
+
+def oracle_ring_grads(q, ks, vs, do, q_pos, k_poss, order=None, q_start=None, scale=None,
+                      chunks=None):
+    """Oracle reference of one rank's ring: the forward over every chunk, then
+    each chunk's gradients and their sums of absolute terms.  Delta comes from
+    the oracle's own O; the forward-error term of the sums is summed over all
+    chunks.  ``chunks`` limits the per-chunk gradients to those indices (the
+    forward and dQ still cover every chunk).  Returns a dict with ``o, lse,
+    delta, dq, mq`` and per-chunk lists ``dk, dv, mk, mv`` (None where not
+    computed)."""
+    import oracle
+    n = len(ks)
+    o, lse = oracle.ring_forward(q, list(ks), list(vs), q_pos, list(k_poss), order=order,
+                                 q_start=q_start, scale=scale)
+    delta = oracle.bwd_delta(o, do)
+    c_all = sum(oracle.attention_abs_dp(q, ks[c], vs[c], do, lse, q_pos, k_poss[c], scale=scale,
+                                        q_start=q_start) for c in range(n))
+    out = {"o": o, "lse": lse, "delta": delta, "dq": 0.0, "mq": 0.0,
+           "dk": [None] * n, "dv": [None] * n, "mk": [None] * n, "mv": [None] * n}
+    for c in range(n):
+        g = oracle.attention_backward(q, ks[c], vs[c], do, lse, delta, q_pos, k_poss[c],
+                                      scale=scale, q_start=q_start)
+        m = oracle.attention_backward_magnitudes(q, ks[c], vs[c], do, o, lse, q_pos, k_poss[c],
+                                                 scale=scale, q_start=q_start, dp_abs=c_all)
+        out["dq"] = out["dq"] + g[0]
+        out["mq"] = out["mq"] + m[0]
+        if chunks is None or c in chunks:
+            out["dk"][c], out["dv"][c], out["mk"][c], out["mv"][c] = g[1], g[2], m[1], m[2]
+    return out

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from long_context_multimodal_amd.workloads import normal_bf16
-from tests.helpers import (assert_close_abs, assert_close_rms, bf16_bits_to_f64, to_dev_bf16,
+from tests.helpers import (assert_close_abs, assert_close_rms, oracle_ring_grads, to_dev_bf16,
                            to_dev_i32, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -103,20 +103,13 @@ def test_packed_ring_forward_backward(mm, lens, p, rank, hq, hkv, d):
     dq, dks, dvs = ring.ring_backward(q, ks, vs, to_dev_bf16(gb), o16, lse, qp_d, kps_d,
                                       rank=rank, q_start=qs_d)
     torch.cuda.synchronize()
-    o_b = bf16_bits_to_f64(to_np(o16))  # delta from the bf16 output, as the GPU path does
-    delta = oracle.bwd_delta(o_b, gv)
-    dq_ref = np.zeros_like(qv, dtype=np.float64)
-    mq_ref = np.zeros_like(dq_ref)
+    ref = oracle_ring_grads(qv, list(kv), list(vv), gv, qp, kps, order=order, q_start=qs)
     for c in range(p):
-        a, bk, bv = oracle.attention_backward(qv, kv[c], vv[c], gv, l_ref, delta, qp, kps[c],
-                                              q_start=qs)
-        mq, mk, mv = oracle.attention_backward_magnitudes(qv, kv[c], vv[c], gv, o_ref, l_ref, qp,
-                                                          kps[c], q_start=qs)
-        dq_ref += a
-        mq_ref += mq
-        assert_close_rms(to_np(dks[c]), bk, bound=mk, what=f"packed dK chunk {c}")
-        assert_close_rms(to_np(dvs[c]), bv, bound=mv, what=f"packed dV chunk {c}")
-    assert_close_rms(to_np(dq), dq_ref, bound=mq_ref, what="packed dQ")
+        assert_close_rms(to_np(dks[c]), ref["dk"][c], bound=ref["mk"][c],
+                         what=f"packed dK chunk {c}")
+        assert_close_rms(to_np(dvs[c]), ref["dv"][c], bound=ref["mv"][c],
+                         what=f"packed dV chunk {c}")
+    assert_close_rms(to_np(dq), ref["dq"], bound=ref["mq"], what="packed dQ")
 
 
 def test_packed_single_sample_equals_plain_causal(mm):

@@ -1,7 +1,8 @@
 """Ring with double-buffered chunk arrival (a second stream copies the next
 KV chunk while the current one is computed; dK/dV are copied out as they are
-produced): it runs the same kernels in the same order as the resident ring,
-so every output must be bit-identical, on repeated calls too."""
+produced): its outputs against the float64 oracle, and -- since it runs the
+same kernels in the same order as the resident ring -- bit-identical to the
+resident ring's, on repeated calls too."""
 
 import numpy as np
 import pytest
@@ -86,3 +87,45 @@ def test_received_ring_matches_resident(mm, rank, fused):
     per_chunk = ks[0].numel() * ks[0].element_size() * 2
     assert rx.bytes_received == 2 * 2 * (len(ks) - 1) * per_chunk
     assert np.isfinite(to_np(l_b)).all()
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_received_ring_matches_oracle(mm, fused):
+    """The double-buffered ring's own outputs -- O, LSE, dQ, and the dK/dV
+    sent back through the copy stream -- against the float64 oracle, every
+    element (rank 1 of P = 4, GQA 8/2, d = 128)."""
+    import torch
+    from long_context_multimodal_amd.workloads import normal_bf16
+    from tests.helpers import (assert_close_abs, assert_close_rms, oracle_ring_grads,
+                               to_dev_bf16, to_dev_i32)
+    mmsp, ring = mm
+    n, p, rank, hq, hkv, d = 4096, 4, 1, 8, 2, 128
+    shard = n // p
+    perm = oracle.zigzag_perm(n, p)
+    qp = perm[rank * shard:(rank + 1) * shard]
+    kps = [perm[c * shard:(c + 1) * shard] for c in range(p)]
+    qb, qv = normal_bf16(121, (shard, hq, d))
+    kb, kv = normal_bf16(122, (p, shard, hkv, d))
+    vb, vv = normal_bf16(123, (p, shard, hkv, d))
+    gb, gv = normal_bf16(124, (shard, hq, d))
+    q, do = to_dev_bf16(qb), to_dev_bf16(gb)
+    ks = [to_dev_bf16(kb[c]) for c in range(p)]
+    vs = [to_dev_bf16(vb[c]) for c in range(p)]
+    kps_d = [to_dev_i32(x) for x in kps]
+    qp_d = kps_d[rank]
+    rx = ring.ChunkReceiver(ks[0], vs[0])
+    dk_sent = [torch.zeros(k.shape, dtype=torch.float32, device=k.device) for k in ks]
+    dv_sent = [torch.zeros(k.shape, dtype=torch.float32, device=k.device) for k in ks]
+    o, lse, o16 = ring.ring_forward_received(q, ks, vs, qp_d, kps_d, rx, rank=rank, fused=fused)
+    dq, _, _ = ring.ring_backward_received(q, ks, vs, do, o16, lse, qp_d, kps_d, rx, rank=rank,
+                                           dk_sent=dk_sent, dv_sent=dv_sent)
+    torch.cuda.synchronize()
+    ref = oracle_ring_grads(qv, list(kv), list(vv), gv, qp, kps, order=ring.ring_order(rank, p))
+    assert_close_abs(to_np(o), ref["o"], what="O")
+    assert_close_abs(to_np(lse), ref["lse"], what="LSE")
+    assert_close_rms(to_np(dq), ref["dq"], bound=ref["mq"], what="dQ")
+    for c in range(p):
+        assert_close_rms(to_np(dk_sent[c]), ref["dk"][c], bound=ref["mk"][c],
+                         what=f"dK sent, chunk {c}")
+        assert_close_rms(to_np(dv_sent[c]), ref["dv"][c], bound=ref["mv"][c],
+                         what=f"dV sent, chunk {c}")

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from long_context_multimodal_amd.workloads import normal_bf16
-from tests.helpers import (assert_close_abs, assert_close_rms, bf16_bits_to_f64, to_dev_bf16,
+from tests.helpers import (assert_close_abs, assert_close_rms, oracle_ring_grads, to_dev_bf16,
                            to_dev_i32, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -104,21 +104,15 @@ def test_training_step_on_rotated_queries_and_keys(mm):
     krv = [oracle.rope_bf16(kv[c], kps[c], 1e7)[1] for c in range(p)]
     assert np.array_equal(to_np(q_rot), oracle.rope_bf16(qv, qp, 1e7)[0])
     order = ring.ring_order(rank, p)
-    o_ref, l_ref = oracle.ring_forward(qrv, krv, list(vv), qp, kps, order=order)
-    assert_close_abs(to_np(o), o_ref, what="O")
-    assert_close_abs(to_np(lse), l_ref, what="LSE")
-    delta = oracle.bwd_delta(bf16_bits_to_f64(to_np(o16)), gv)
-    dq_ref = np.zeros((shard, hq, d))
-    mq_ref = np.zeros((shard, hq, d))
+    ref = oracle_ring_grads(qrv, krv, list(vv), gv, qp, kps, order=order)
+    assert_close_abs(to_np(o), ref["o"], what="O")
+    assert_close_abs(to_np(lse), ref["lse"], what="LSE")
     for c in range(p):
-        a, bk, bv = oracle.attention_backward(qrv, krv[c], vv[c], gv, l_ref, delta, qp, kps[c])
-        mq, mk, mv = oracle.attention_backward_magnitudes(qrv, krv[c], vv[c], gv, o_ref, l_ref,
-                                                          qp, kps[c])
-        dq_ref += a
-        mq_ref += mq
-        dk_ref = oracle.rope(bk, kps[c], 1e7, inverse=True)
-        assert_close_rms(to_np(dks[c]), dk_ref, bound=_pair_sum(mk), what=f"dK chunk {c}")
-        assert_close_rms(to_np(dvs[c]), bv, bound=mv, what=f"dV chunk {c}")
+        dk_ref = oracle.rope(ref["dk"][c], kps[c], 1e7, inverse=True)
+        assert_close_rms(to_np(dks[c]), dk_ref, bound=_pair_sum(ref["mk"][c]),
+                         what=f"dK chunk {c}")
+        assert_close_rms(to_np(dvs[c]), ref["dv"][c], bound=ref["mv"][c], what=f"dV chunk {c}")
+    dq_ref, mq_ref = ref["dq"], ref["mq"]
     assert_close_rms(to_np(dq), oracle.rope(dq_ref, qp, 1e7, inverse=True),
                      bound=_pair_sum(mq_ref), what="dQ")
 

@@ -1,0 +1,118 @@
+"""GPU parity at launch shapes that reach every branch of the workgroup ->
+tile order, every element against the float64 oracle.
+
+The order (heavy tiles first; when one head's tiles span several XCDs, heavy
+and light tiles alternate in blocks of 8) has three regimes per kernel: whole
+heads per XCD, two or more blocks of 8 per head, and the 2M-token per-GPU
+share's 512 tiles per head over 4 heads.  The full-size runs of that share can
+check dK/dV only at a few keys, so the last two cases here reproduce its
+tiling exactly -- 512 key tiles of 128 per KV head for the dK/dV kernel, 512
+query tiles of 128 (256 of 256 for the forward) per query head for the dQ and
+forward kernels -- with few enough rows (or keys) on the other side for the
+oracle to check every element.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_multimodal_amd.workloads import normal_bf16
+from tests.helpers import (assert_close_abs, assert_close_rms, oracle_ring_grads, to_dev_bf16,
+                           to_dev_i32, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from long_context_multimodal_amd import mmsp, ring
+    mmsp.lib()
+    return mmsp, ring
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_ring_with_alternating_tile_blocks(mm, packed):
+    """Rank 1 of P = 4 over 16,384 tokens, GQA 4/2, d = 128: per chunk 32 key
+    tiles per KV head on a grid of 64 (dK/dV), 32 query tiles per head on 128
+    (dQ) and 16 on 64 (forward) -- each alternates blocks of 8.  Plain causal
+    and packed clips (each zigzagged over the 4 ranks)."""
+    mmsp, ring = mm
+    import torch
+    n, p, rank, hq, hkv, d = 16384, 4, 1, 4, 2, 128
+    shard = n // p
+    qs = qs_d = None
+    if packed:
+        starts = np.array([0, 2048, 2560, 9216, 10240, n], dtype=np.int32)
+        perm, first = oracle.zigzag_packed_perm(starts, p)
+        qs = first[rank * shard:(rank + 1) * shard].astype(np.int32)
+        qs_d = to_dev_i32(qs)
+    else:
+        perm = oracle.zigzag_perm(n, p)
+    qp = perm[rank * shard:(rank + 1) * shard].astype(np.int32)
+    kps = [perm[c * shard:(c + 1) * shard].astype(np.int32) for c in range(p)]
+    seed = 300 + 10 * packed
+    qb, qv = normal_bf16(seed, (shard, hq, d))
+    kb, kv = normal_bf16(seed + 1, (p, shard, hkv, d))
+    vb, vv = normal_bf16(seed + 2, (p, shard, hkv, d))
+    gb, gv = normal_bf16(seed + 3, (shard, hq, d))
+    q = to_dev_bf16(qb)
+    ks = [to_dev_bf16(kb[c]) for c in range(p)]
+    vs = [to_dev_bf16(vb[c]) for c in range(p)]
+    qp_d = to_dev_i32(qp)
+    kps_d = [to_dev_i32(x) for x in kps]
+    o, lse, o16 = ring.ring_forward(q, ks, vs, qp_d, kps_d, rank=rank, q_start=qs_d)
+    dq, dks, dvs = ring.ring_backward(q, ks, vs, to_dev_bf16(gb), o16, lse, qp_d, kps_d,
+                                      rank=rank, q_start=qs_d)
+    torch.cuda.synchronize()
+    ref = oracle_ring_grads(qv, list(kv), list(vv), gv, qp, kps, order=ring.ring_order(rank, p),
+                            q_start=qs)
+    assert_close_abs(to_np(o), ref["o"], what="O")
+    assert_close_abs(to_np(lse), ref["lse"], what="LSE")
+    for c in range(p):
+        assert_close_rms(to_np(dks[c]), ref["dk"][c], bound=ref["mk"][c], what=f"dK chunk {c}")
+        assert_close_rms(to_np(dvs[c]), ref["dv"][c], bound=ref["mv"][c], what=f"dV chunk {c}")
+    assert_close_rms(to_np(dq), ref["dq"], bound=ref["mq"], what="dQ")
+
+
+def _chain_vs_oracle(mm, qp, kp, hq, hkv, d, seed):
+    """GPU forward -> bf16 O -> preprocess -> backward of one chunk, every
+    element against the oracle (delta from the oracle's own O)."""
+    mmsp, _ = mm
+    import torch
+    sq, sk = len(qp), len(kp)
+    qb, qv = normal_bf16(seed, (sq, hq, d))
+    kb, kv = normal_bf16(seed + 1, (sk, hkv, d))
+    vb, vv = normal_bf16(seed + 2, (sk, hkv, d))
+    gb, gv = normal_bf16(seed + 3, (sq, hq, d))
+    q, k, v, do = (to_dev_bf16(x) for x in (qb, kb, vb, gb))
+    qp_d, kp_d = to_dev_i32(qp), to_dev_i32(kp)
+    o, lse = mmsp.attn_fwd_chunk(q, k, v, qp_d, kp_d)
+    delta = mmsp.attn_bwd_preprocess(o.to(torch.bfloat16), do)
+    dq = torch.zeros((sq, hq, d), dtype=torch.float32, device="cuda")
+    dk, dv = mmsp.attn_bwd_chunk(q, k, v, do, lse, delta, qp_d, kp_d, dq)
+    torch.cuda.synchronize()
+    ref = oracle_ring_grads(qv, [kv], [vv], gv, qp, [kp])
+    assert_close_abs(to_np(o), ref["o"], what="O")
+    assert_close_abs(to_np(lse), ref["lse"], what="LSE")
+    assert_close_rms(to_np(dq), ref["dq"], bound=ref["mq"], what="dQ")
+    assert_close_rms(to_np(dk), ref["dk"][0], bound=ref["mk"][0], what="dK")
+    assert_close_rms(to_np(dv), ref["dv"][0], bound=ref["mv"][0], what="dV")
+
+
+def test_dkdv_tiling_of_the_2m_share(mm):
+    """65,536 keys x 4 KV heads (512 key tiles per head on a grid of 2048,
+    64 blocks of 8 alternating), against 512 queries at positions 128 i + 127,
+    so every key tile is seen by a different number of rows."""
+    qp = (np.arange(512) * 128 + 127).astype(np.int32)
+    kp = np.arange(65536, dtype=np.int32)
+    _chain_vs_oracle(mm, qp, kp, 4, 4, 128, seed=400)
+
+
+def test_dq_and_forward_tiling_of_the_2m_share(mm):
+    """65,536 queries x 4 heads (dQ: 512 query tiles per head on a grid of
+    2048; forward: 256 on 1024) against 512 keys at positions 128 j."""
+    qp = np.arange(65536, dtype=np.int32)
+    kp = (np.arange(512) * 128).astype(np.int32)
+    _chain_vs_oracle(mm, qp, kp, 4, 4, 128, seed=410)
