@@ -24,7 +24,9 @@
  *
  *  - Every data pointer is a DEVICE pointer owned by the caller; the library
  *    keeps no pointer after the call returns and allocates no device memory
- *    (scratch comes from the caller, sized by a *_workspace_bytes query).
+ *    (scratch comes from the caller, sized by a *_workspace_bytes query; the
+ *    one exception, mmsp_shard_balance_noalloc, uses a static array of the
+ *    library's code object instead).
  *  - bf16 tensors are passed as `const void*` holding IEEE bfloat16 bits.
  *    Layouts are row-major and contiguous: token-major activations
  *    [tokens][heads][head_dim]; per-head statistics [heads][tokens].
@@ -33,8 +35,8 @@
  *    next synchronisation of that stream.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    nonzero return means nothing was launched.  Calls are thread-safe and
- *    keep no global device state.  Position arrays must be strictly
- *    increasing (a precondition, not checked).
+ *    keep no global device state (but for that static array).  Position
+ *    arrays must be strictly increasing (a precondition, not checked).
  *  - No entry point allocates, synchronises or enqueues a memset (buffers
  *    that must start at zero are cleared by the library's own kernels), so
  *    the enqueued work can be captured in a HIP graph; the host-only
@@ -103,6 +105,26 @@ size_t mmsp_shard_balance_workspace_bytes(int64_t n, int32_t n_ranks, int32_t mo
 int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
                        int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
                        void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* ---- a1 without allocation ---------------------------------------------------
+ * For callers that cannot allocate device memory or hand over a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same permutation as mmsp_shard_balance, bit for bit, with
+ * MODALITY's scratch taken from an array the library holds in each device's
+ * memory (2 * MMSP_NOALLOC_MAX_BLOCKS int32, 512 KiB, kept until the process
+ * ends).  Arguments and checks are those of mmsp_shard_balance, less the
+ * workspace; MODALITY with n / granularity > MMSP_NOALLOC_MAX_BLOCKS returns
+ * MMSP_ERR_WORKSPACE.  The current device must be the stream's device: the
+ * array's address is looked up (hipGetSymbolAddress) on the first call on
+ * each device; MMSP_ERR_HIP if that fails.  Calls on one device share the
+ * array, so two calls whose work may overlap on that device (two streams,
+ * two threads) race; calls ordered on one stream do not.  Nothing in the
+ * array needs to start at zero: every call writes what it reads.
+ */
+#define MMSP_NOALLOC_MAX_BLOCKS 65536
+int mmsp_shard_balance_noalloc(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
+                               int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
+                               void* stream);
 
 /* ---- a1 for packed samples: per-sample zigzag ------------------------------
  * Variable-length videos packed into one buffer with reset attention masks

@@ -12,6 +12,8 @@ namespace {
 
 constexpr long long kMaxElems = 0x7fffffffLL;  // element offsets stay in int32 range per row
 constexpr int kMaxRanks = 1024;
+static_assert(MMSP_NOALLOC_MAX_BLOCKS == mmsp::kNoallocMaxBlocks,
+              "header and library agree on the static scratch size");
 
 inline bool bad_dim(int32_t d) { return d != 64 && d != 128; }
 
@@ -153,24 +155,52 @@ size_t mmsp_shard_balance_workspace_bytes(int64_t n, int32_t n_ranks, int32_t mo
   return (size_t)(2 * n_blocks) * sizeof(int32_t);
 }
 
-int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
-                       int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
-                       void* d_workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// host checks shared by the two shard-balance entry points
+int check_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
+                  int32_t granularity, const int32_t* d_perm) {
   if (mode != MMSP_BALANCE_ZIGZAG && mode != MMSP_BALANCE_MODALITY) return MMSP_ERR_UNSUPPORTED;
   if (d_perm == nullptr) return MMSP_ERR_NULL;
   if (mode == MMSP_BALANCE_MODALITY && d_labels == nullptr) return MMSP_ERR_NULL;
   if (n <= 0 || n > kMaxElems || n_ranks <= 0 || n_ranks > kMaxRanks) return MMSP_ERR_SHAPE;
-  int32_t* ws_vis = nullptr;
-  int32_t* ws_owner = nullptr;
   if (mode == MMSP_BALANCE_ZIGZAG) {
     if (n % (2LL * n_ranks) != 0) return MMSP_ERR_DIVISIBILITY;
   } else {
     if (granularity <= 0) return MMSP_ERR_SHAPE;
     if (n % (2LL * n_ranks * granularity) != 0) return MMSP_ERR_DIVISIBILITY;
+  }
+  return MMSP_OK;
+}
+}  // namespace
+
+int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
+                       int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
+                       void* d_workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_balance(d_labels, n, n_ranks, mode, granularity, d_perm);
+  if (st != MMSP_OK) return st;
+  int32_t* ws_vis = nullptr;
+  int32_t* ws_owner = nullptr;
+  if (mode == MMSP_BALANCE_MODALITY) {
     const size_t need = mmsp_shard_balance_workspace_bytes(n, n_ranks, mode, granularity);
     if (d_workspace == nullptr || workspace_bytes < need) return MMSP_ERR_WORKSPACE;
     ws_vis = static_cast<int32_t*>(d_workspace);
     ws_owner = ws_vis + n / granularity;
+  }
+  return check_hip(mmsp::launch_shard_balance(d_labels, (int)n, n_ranks, mode, granularity,
+                                              d_perm, d_inv_perm, ws_vis, ws_owner,
+                                              as_stream(stream)));
+}
+
+int mmsp_shard_balance_noalloc(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
+                               int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
+                               void* stream) {
+  const int st = check_balance(d_labels, n, n_ranks, mode, granularity, d_perm);
+  if (st != MMSP_OK) return st;
+  int32_t* ws_vis = nullptr;
+  int32_t* ws_owner = nullptr;
+  if (mode == MMSP_BALANCE_MODALITY) {
+    if (n / granularity > MMSP_NOALLOC_MAX_BLOCKS) return MMSP_ERR_WORKSPACE;
+    if (mmsp::noalloc_balance_scratch(&ws_vis, &ws_owner) != hipSuccess) return MMSP_ERR_HIP;
   }
   return check_hip(mmsp::launch_shard_balance(d_labels, (int)n, n_ranks, mode, granularity,
                                               d_perm, d_inv_perm, ws_vis, ws_owner,

@@ -60,6 +60,12 @@ hipError_t launch_shard_balance(const uint8_t* labels, int n, int n_ranks, int m
                                 int32_t* perm, int32_t* inv_perm, int32_t* ws_vis,
                                 int32_t* ws_owner, hipStream_t stream);
 
+// Allocation-free variant: the device address, on the current device, of the
+// library's own static scratch (vis, then owner, kNoallocMaxBlocks int32 each),
+// looked up once per device.
+constexpr int kNoallocMaxBlocks = 1 << 16;
+hipError_t noalloc_balance_scratch(int32_t** vis, int32_t** owner);
+
 // per-sample zigzag of packed samples (starts: n_samples + 1 positions)
 hipError_t launch_shard_balance_packed(const int32_t* starts, int n_samples, int n, int n_ranks,
                                        int32_t* perm, int32_t* inv_perm, int32_t* token_start,

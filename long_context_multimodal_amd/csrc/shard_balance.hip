@@ -28,11 +28,21 @@
 // block ? 0 : L_s) + o % L_s.  One thread per token: a fill kernel first sets
 // every slot to -1, then tokens of samples with valid boundaries are placed.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace mmsp {
+
+// Scratch of the allocation-free MODALITY balance (mmsp_shard_balance_noalloc):
+// the per-block visual counts, then the per-block owners, kNoallocMaxBlocks
+// int32 each.  Every device the library runs on holds its own copy until the
+// process ends, and every call on that device shares it.  Host code never
+// passes this name to a kernel: it is a host-side stand-in, and the device
+// address comes from hipGetSymbolAddress (noalloc_balance_scratch below).
+static __device__ __align__(256) int32_t scratch[2 * kNoallocMaxBlocks];
+
 namespace {
 
 __global__ void __launch_bounds__(64) block_visual_kernel(const uint8_t* __restrict__ labels,
@@ -225,6 +235,29 @@ hipError_t launch_shard_balance_packed(const int32_t* starts, int n_samples, int
   hipLaunchKernelGGL(packed_scatter_kernel, grid, dim3(256), 0, stream, n, n_ranks, starts,
                      n_samples, perm, inv_perm, token_start);
   return hipGetLastError();
+}
+
+hipError_t noalloc_balance_scratch(int32_t** vis, int32_t** owner) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {  // once per device, with that device current
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      addr[dev] = p;
+    }
+    p = addr[dev];
+  }
+  *vis = static_cast<int32_t*>(p);
+  *owner = static_cast<int32_t*>(p) + kNoallocMaxBlocks;
+  return hipSuccess;
 }
 
 hipError_t launch_shard_balance(const uint8_t* labels, int n, int n_ranks, int mode, int g,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "mmsp_attn_bwd_preprocess": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP]),
     "mmsp_attn_bwd_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
                                            _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
+    "mmsp_shard_balance_noalloc": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP]),
     "mmsp_shard_balance_packed": (ctypes.c_int, [_VP, _I32, _I64, _I32, _VP, _VP, _VP, _VP]),
     "mmsp_shard_gather": (ctypes.c_int, [_VP, _I64, _VP, _I64, _I64, _VP, _VP]),
     "mmsp_check_positions": (ctypes.c_int, [_VP, _VP, _I32, _VP, _VP]),
@@ -157,6 +158,24 @@ def shard_balance(n: int, n_ranks: int, mode: int = BALANCE_ZIGZAG, granularity:
     _check(lib().mmsp_shard_balance(_ptr(labels), n, n_ranks, mode, granularity, _ptr(perm),
                                     _ptr(inv), _ptr(ws), ws_bytes, _stream()),
            "mmsp_shard_balance")
+    return perm, inv
+
+
+def shard_balance_noalloc(perm, n_ranks: int, mode: int = BALANCE_ZIGZAG, granularity: int = 0,
+                          labels=None, inv=None):
+    """``shard_balance`` into caller-given ``perm`` (and ``inv``), int32[n], with
+    the library's own scratch (``mmsp_shard_balance_noalloc``): nothing is
+    allocated."""
+    import torch
+    _need(perm, torch.int32, "perm", 1)
+    n = perm.numel()
+    _need(inv, torch.int32, "inv", 1)
+    _shape(inv, (n,), "inv")
+    _need(labels, torch.uint8, "labels", 1)
+    _shape(labels, (n,), "labels")
+    _check(lib().mmsp_shard_balance_noalloc(_ptr(labels), n, n_ranks, mode, granularity,
+                                            _ptr(perm), _ptr(inv), _stream()),
+           "mmsp_shard_balance_noalloc")
     return perm, inv
 
 

@@ -288,3 +288,15 @@ def test_native_program_rejects_bad_input(tmp_path):
     assert r.returncode == 1 and "bad header" in r.stderr
     r = subprocess.run([TOOL], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr
+
+
+def test_shard_balance_noalloc_rejects():
+    lib = mmsp.lib()
+    f = lib.mmsp_shard_balance_noalloc
+    assert f(FAKE, 1024, 4, 1, 16, None, None, None) == -1      # no perm
+    assert f(None, 1024, 4, 1, 16, FAKE, None, None) == -1      # MODALITY needs labels
+    assert f(FAKE, 1024, 4, 7, 16, FAKE, None, None) == -3      # unknown mode
+    assert f(FAKE, 0, 4, 0, 0, FAKE, None, None) == -2
+    assert f(FAKE, 1000, 4, 1, 16, FAKE, None, None) == -4      # not a multiple of 2*P*g
+    # past the static scratch: 131,072 blocks of 16 tokens
+    assert f(FAKE, 1 << 21, 8, 1, 16, FAKE, None, None) == -5
