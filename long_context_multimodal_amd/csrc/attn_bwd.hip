@@ -60,11 +60,15 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char sQ0[C::TILE], sQ1[C::TILE];
   __shared__ __attribute__((aligned(16))) char sO0[C::TILE], sO1[C::TILE];
   __shared__ __attribute__((aligned(16))) char sVrows[C::VTILE];
-  __shared__ __attribute__((aligned(16))) float sL[2][C::BQ];      // LSE*log2e (+inf empty)
-  __shared__ __attribute__((aligned(16))) float sDl[2][C::BQ];     // delta
-  __shared__ __attribute__((aligned(16))) int sQp[2][C::BQ];       // positions
-  __shared__ __attribute__((aligned(16))) int sQs[2][C::BQ];       // sample starts (packed)
-  __shared__ int sQlast[2];
+  // per-row statistics of the two tiles in flight, one row of 36 words per
+  // (statistic, buffer): 0 sample starts (packed), 1 LSE*log2e (+inf empty),
+  // 2 delta, 3 positions (word 32: the tile's last position)
+  constexpr int SROW = 36;
+  __shared__ __attribute__((aligned(16))) uint32_t sStat[4][2][SROW];
+  auto sQs = [&](int b) -> const int* { return (const int*)sStat[0][b]; };
+  auto sL = [&](int b) -> const float* { return (const float*)sStat[1][b]; };
+  auto sDl = [&](int b) -> const float* { return (const float*)sStat[2][b]; };
+  auto sQp = [&](int b) -> const int* { return (const int*)sStat[3][b]; };
   auto qtile = [&](auto b) -> lds_char* {
     if constexpr (decltype(b)::value == 0) return (lds_char*)sQ0; else return (lds_char*)sQ1;
   };
@@ -175,50 +179,50 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   // 1: LSE, 2: delta, 3: positions, its lane BQ fetching the tile's last
   // position), all into the one register `stat`; the array and its per-head
   // stride are fixed per wave before the loop.
-  const uint32_t* stat_src = wave == 0   ? (const uint32_t*)p.q_start
-                             : wave == 1 ? (const uint32_t*)p.lse
-                             : wave == 2 ? (const uint32_t*)p.delta
-                             : p.causal  ? (const uint32_t*)p.q_pos
-                                         : (const uint32_t*)p.lse;  // any readable row
+  const uint32_t* stat_src = (wave == 0 && packed) ? (const uint32_t*)p.q_start
+                             : wave == 2           ? (const uint32_t*)p.delta
+                             : (wave == 3 && p.causal) ? (const uint32_t*)p.q_pos
+                                                   : (const uint32_t*)p.lse;  // any readable row
   const size_t stat_head = (wave == 1 || wave == 2) ? (size_t)p.sq : 0;
-  auto issue_next = [&](auto buf) {
-    const int h = nx_h, q0 = nx_q0;
+  // Loads of the next tile, without branches, so that the scheduler can
+  // spread them between the contractions of the current one (issued all at
+  // once they queue behind the other waves' at the texture unit).  With no
+  // next tile (`live` false) the buffer ranges are empty: the loads fetch
+  // nothing and fill the unused buffer with zeros.
+  auto issue_next = [&](auto buf, bool live) {
+    const int h = min(nx_h, p.hq - 1), q0 = nx_q0;
     const size_t o = nx_off;
-    nx_q0 += C::BQ;
-    nx_off += tile_step;
-    if (nx_q0 >= n_qt * C::BQ) {
-      nx_q0 = qt0 * C::BQ;
-      ++nx_h;
-      nx_off -= head_back;
-    }
-    if (q0 + C::BQ <= p.sq) {
-      ld.load(qtile(buf), p.q + o);
-      ld.load(otile(buf), p.dout + o);
-    } else {
-      ld.load_clamped(qtile(buf), p.q + o, q_row_stride, p.sq - q0);
-      ld.load_clamped(otile(buf), p.dout + o, q_row_stride, p.sq - q0);
-    }
+    const bool wrap = nx_q0 + C::BQ >= n_qt * C::BQ;
+    nx_q0 = wrap ? qt0 * C::BQ : nx_q0 + C::BQ;
+    nx_h = wrap ? nx_h + 1 : nx_h;
+    nx_off = wrap ? nx_off + tile_step - head_back : nx_off + tile_step;
+    const int rows = uniform(live ? min(C::BQ, p.sq - q0) : 0);
+    ld.load_clamped(qtile(buf), p.q + o, q_row_stride, rows);
+    ld.load_clamped(otile(buf), p.dout + o, q_row_stride, rows);
     // Raw values only: they are converted when published, after the wait
     // that ends the step, so no load here is waited for inside the step.
-    if ((wave != 0 || packed) && lane <= C::BQ) {
-      const int i = min(q0 + min(lane, C::BQ - 1), p.sq - 1);
-      stat = stat_src[(size_t)h * stat_head + i];
-      row_live = q0 + lane < p.sq;
-    }
+    const int i = min(q0 + min(lane, C::BQ - 1), p.sq - 1);
+    stat = stat_src[(size_t)h * stat_head + i];
+    row_live = q0 + lane < p.sq;
   };
+  // Each wave converts its statistic and writes it with one store: the
+  // destination row is fixed per wave, so only the lane offset is a register.
   auto publish_tile = [&](int buf) {
-    if (wave == 0 && lane < C::BQ) {
-      sQs[buf][lane] = (packed && row_live) ? (int)stat : INT_MIN;
-    } else if (wave == 1 && lane < C::BQ) {
-      // empty rows (LSE = -inf) and rows past sq get P = exp2(s c - inf) = 0
-      const float l = __uint_as_float(stat);
-      sL[buf][lane] = (row_live && l != -INFINITY) ? l * kLog2e : INFINITY;
-    } else if (wave == 2 && lane < C::BQ) {
-      sDl[buf][lane] = row_live ? __uint_as_float(stat) : 0.f;
-    } else if (wave == 3 && lane <= C::BQ) {
-      const int pos = p.causal ? (int)stat : kPosInf - 1;
-      if (lane < C::BQ) sQp[buf][lane] = row_live ? pos : INT_MIN;
-      else sQlast[buf] = pos;
+    if (lane <= C::BQ && (wave == 3 || lane < C::BQ)) {
+      uint32_t val;
+      if (wave == 0) {
+        val = (packed && row_live) ? stat : (uint32_t)INT_MIN;
+      } else if (wave == 1) {
+        // empty rows (LSE = -inf) and rows past sq get P = exp2(s c - inf) = 0
+        const float l = __uint_as_float(stat);
+        val = __float_as_uint((row_live && l != -INFINITY) ? l * kLog2e : INFINITY);
+      } else if (wave == 2) {
+        val = row_live ? stat : 0u;
+      } else {
+        const int pos = p.causal ? (int)stat : kPosInf - 1;
+        val = (uint32_t)((row_live || lane == C::BQ) ? pos : INT_MIN);
+      }
+      sStat[wave][buf][lane] = val;
     }
   };
 
@@ -233,14 +237,17 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   auto step = [&](auto buf_tag, int it) {
     constexpr int BUF = decltype(buf_tag)::value;
     using Next = std::integral_constant<int, BUF ^ 1>;
-    if (it + 1 < total) issue_next(Next{});
+    const bool more = it + 1 < total;
     const lds_char* qt = qtile(buf_tag);
     const lds_char* dt = otile(buf_tag);
-    const int qfirst = uniform(sQp[BUF][0]);
-    const int qlast = uniform(sQlast[BUF]);
-    const int qs_first = packed ? uniform(sQs[BUF][0]) : INT_MIN;
-    const int qs_last = packed ? uniform(sQs[BUF][C::BQ - 1]) : INT_MIN;
-    if (wave_live && qlast >= wkmin && qs_first <= wkmax) {
+    const int qfirst = uniform(sQp(BUF)[0]);
+    const int qs_last = packed ? uniform(sQs(BUF)[C::BQ - 1]) : INT_MIN;
+    // Every wave runs every tile: one whose keys the tile's rows cannot see
+    // (only next to the causal diagonal) masks all its scores and adds zeros.
+    // Without a branch here, the next tile's loads share one scheduling
+    // region with the contractions below.
+    {
+      issue_next(Next{}, more);
       // S = Q K^T and dP = dO V^T  (row = query, col = key)
       f32x16 s = mfma32x32x16(lds_read_b128(qt, qoff[0]), kf[0], f32x16{});
       f32x16 dp = mfma32x32x16(lds_read_b128(dt, qoff[0]), lds_read_b128(vrows, qoff[0]),
@@ -250,15 +257,22 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
         s = mfma32x32x16(lds_read_b128(qt, qoff[ks]), kf[ks], s);
         dp = mfma32x32x16(lds_read_b128(dt, qoff[ks]), lds_read_b128(vrows, qoff[ks]), dp);
       }
-      const int last_row_pos = uniform(sQp[BUF][C::BQ - 1]);  // INT_MIN past sq
+      // the next tile's loads spread between the contractions, one after
+      // every other one, instead of queueing at the texture unit all at once
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      const int last_row_pos = uniform(sQp(BUF)[C::BQ - 1]);  // INT_MIN past sq
       // straddles the rows' positions or their sample starts (or the tail)
       if (!(wave_full_keys && qfirst >= wkmax && last_row_pos != INT_MIN && qs_last <= wkmin)) {
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int q = 8 * (i >> 2) + 4 * hh + (i & 3);
-          bool hide = kpos > sQp[BUF][q];
-          if constexpr (packed) hide |= kpos < sQs[BUF][q];
+          bool hide = kpos > sQp(BUF)[q];
+          if constexpr (packed) hide |= kpos < sQs(BUF)[q];
           s[i] = hide ? -INFINITY : s[i];
         }
       }
@@ -266,8 +280,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int q = 8 * g + 4 * hh;  // rows q .. q+3 of this lane
-        const f32x4 lq = *(const f32x4*)&sL[BUF][q];
-        const f32x4 dq = *(const f32x4*)&sDl[BUF][q];
+        const f32x4 lq = *(const f32x4*)&sL(BUF)[q];
+        const f32x4 dq = *(const f32x4*)&sDl(BUF)[q];
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -306,7 +320,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    if (it + 1 < total) {
+    if (more) {
       publish_tile(BUF ^ 1);
       wait_vmem();
     }
@@ -314,7 +328,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   };
 
   if (total > 0) {
-    issue_next(B0{});
+    issue_next(B0{}, true);
     publish_tile(0);
   }
   wait_vmem();
@@ -325,25 +339,67 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   }
 
   // ---- epilogue: dK = scale * (dK^T)^T, dV = (dV^T)^T ----
-  if (!key_ok) return;
-  float* dkr = p.dk + (size_t)key * kv_stride + (size_t)kvh * D;
-  float* dvr = p.dv + (size_t)key * kv_stride + (size_t)kvh * D;
+  // A lane holds one key's head-dim entries in 16-byte pieces that sit 32
+  // bytes apart, so storing them directly writes each row in 32-byte pieces.
+  // Each wave instead passes its 32 keys through LDS (free after the loop's
+  // last barrier) and writes whole rows: a store of 64 lanes x 16 bytes covers
+  // 1 KiB of consecutive rows.  The accumulator's 16-byte pieces are dumped
+  // as they are, one 1 KiB block per (32-column block, 8-row group) with lane
+  // L's piece in slot L ^ block, so the dump is a plain 1 KiB write and the
+  // 32 lanes that later read one row's pieces hit 16 different bank groups.
+  if (!wave_live) return;
+  constexpr int NB = C::MB * 4;          // 1 KiB blocks per accumulator
+  constexpr int CH = D / 4;              // 16-byte pieces per fp32 row
+  constexpr int READS = 32 * CH / kWave; // pieces per lane
+  static_assert(NB / 2 * 1024 <= C::TILE, "half the blocks fit one Q/dO tile buffer");
+  lds_char* reg0;
+  lds_char* reg1;  // blocks [0, NB/2) and [NB/2, NB) of this wave
+  if (wave < 2) {
+    reg0 = (lds_char*)sVrows + wave * NB * 1024;
+    reg1 = reg0 + NB / 2 * 1024;
+  } else if (wave == 2) {
+    reg0 = (lds_char*)sQ0;
+    reg1 = (lds_char*)sQ1;
+  } else {
+    reg0 = (lds_char*)sO0;
+    reg1 = (lds_char*)sO1;
+  }
+  // the piece a lane reads in step i: row rr = (i * 64 + lane) / CH of the
+  // wave's 32 keys, columns 4 cc .. 4 cc + 3, cc = lane % CH, which lives in
+  // block b = cc / 2 (mb = b / 4, g = b % 4), lane slot (cc % 2) * 32 + rr
+  const int cc = lane % CH;
+  const int rb = cc >> 1;
+  lds_char* rbase = (rb < NB / 2 ? reg0 + rb * 1024 : reg1 + (rb - NB / 2) * 1024);
+  auto store_rows = [&](const f32x16* acc, float mul, float* out) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
+    for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = mb * 32 + 8 * g + 4 * hh;
-      f32x4 kv4 = {dkacc[mb][4 * g] * p.scale, dkacc[mb][4 * g + 1] * p.scale,
-                   dkacc[mb][4 * g + 2] * p.scale, dkacc[mb][4 * g + 3] * p.scale};
-      f32x4 vv4 = {dvacc[mb][4 * g], dvacc[mb][4 * g + 1], dvacc[mb][4 * g + 2],
-                   dvacc[mb][4 * g + 3]};
-      if (p.accumulate) {
-        kv4 += *(const f32x4*)(dkr + d0);
-        vv4 += *(const f32x4*)(dvr + d0);
+      for (int g = 0; g < 4; ++g) {
+        const int b = mb * 4 + g;
+        lds_char* blk = (b < NB / 2 ? reg0 + b * 1024 : reg1 + (b - NB / 2) * 1024);
+        const f32x4 v4 = {acc[mb][4 * g] * mul, acc[mb][4 * g + 1] * mul,
+                          acc[mb][4 * g + 2] * mul, acc[mb][4 * g + 3] * mul};
+        *(__attribute__((address_space(3))) f32x4*)(blk + ((lane ^ b) << 4)) = v4;
       }
-      *(f32x4*)(dkr + d0) = kv4;
-      *(f32x4*)(dvr + d0) = vv4;
+    wait_lds_writes();
+#pragma unroll
+    for (int i = 0; i < READS; ++i) {
+      const int rr = (i * kWave + lane) / CH;
+      const int slot = ((cc & 1) << 5) | rr;
+      const f32x4 v4 =
+          *(const __attribute__((address_space(3))) f32x4*)(rbase + ((slot ^ rb) << 4));
+      const int k = wk0 + rr;
+      if (k < p.sk) {
+        float* dst = out + (size_t)k * kv_stride + (size_t)kvh * D + cc * 4;
+        f32x4 w = v4;
+        if (p.accumulate) w += *(const f32x4*)dst;
+        *(f32x4*)dst = w;
+      }
     }
+  };
+  store_rows(dkacc, p.scale, p.dk);
+  wait_lds_writes();  // the reads of dK's pieces are done before dV's dump reuses the blocks
+  store_rows(dvacc, 1.0f, p.dv);
 }
 
 // ================================== dQ =======================================
@@ -470,20 +526,18 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   ld.init(tid, kv_row_stride);
   int kpreg = kPosInf;
   bool key_live = false;
-  auto issue_tile = [&](int t, auto buf) {
+  // Loads of tile t without branches (see the dK/dV kernel): with `live`
+  // false the ranges are empty and nothing is fetched.  Every thread reads a
+  // position (clamped into the array); threads below BN publish theirs.
+  auto issue_tile = [&](int t, auto buf, bool live) {
     const int j0 = (tb + t) * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
-    if (j0 + C::BN <= p.sk) {
-      ld.load(ktile(buf), kbase + o);
-      ld.load(vtile(buf), vbase + o);
-    } else {
-      ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, p.sk - j0);
-      ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, p.sk - j0);
-    }
-    if (tid < C::BN) {  // raw position; keys past sk are hidden when published
-      kpreg = p.causal ? p.k_pos[min(j0 + tid, p.sk - 1)] : 0;
-      key_live = j0 + tid < p.sk;
-    }
+    const int rows = uniform(live ? min(C::BN, p.sk - j0) : 0);
+    ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, rows);
+    ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, rows);
+    // raw position; keys past sk are hidden when published
+    kpreg = p.causal ? p.k_pos[max(0, min(j0 + (tid & (C::BN - 1)), p.sk - 1))] : 0;
+    key_live = j0 + (tid & (C::BN - 1)) < p.sk;
   };
 
   f32x16 dqacc[C::MB];
@@ -494,24 +548,36 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   auto step = [&](auto buf_tag, int t) {
     constexpr int BUF = decltype(buf_tag)::value;
     using Next = std::integral_constant<int, BUF ^ 1>;
-    if (t + 1 < nt) issue_tile(t + 1, Next{});
+    const bool more = t + 1 < nt;
     const lds_char* kt = ktile(buf_tag);
     const lds_char* vt = vtile(buf_tag);
     const int* kp = kpos_of(buf_tag);
     const int kfirst = uniform(kp[0]);
     const int klast = uniform(kp[C::BN - 1]);
-    if (wave_live && kfirst <= wqmax && klast >= wqs_min) {
+    // Every wave runs every tile: one whose rows cannot see it (only next to
+    // the causal diagonal, or rows past sq) takes the masked path, which
+    // hides all its keys, and adds zeros.
+    {
       // straddles the rows' positions or their sample starts
-      const bool straddle = klast > wqmin || kfirst < wqs_max;
+      const bool straddle = !wave_live || klast > wqmin || kfirst < wqs_max;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {  // 32 keys at a time
         const int rb = kb * 32 * D * 2;
+        if (kb == 0) issue_tile(t + 1, Next{}, more);
         f32x16 s = mfma32x32x16(lds_read_b128(kt, rb + koff[0]), qf[0], f32x16{});
         f32x16 dp = mfma32x32x16(lds_read_b128(vt, rb + koff[0]), df[0], f32x16{});
 #pragma unroll
         for (int ks = 1; ks < C::KS; ++ks) {
           s = mfma32x32x16(lds_read_b128(kt, rb + koff[ks]), qf[ks], s);
           dp = mfma32x32x16(lds_read_b128(vt, rb + koff[ks]), df[ks], dp);
+        }
+        if (kb == 0) {
+          // the next tile's loads spread between the contractions
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
         }
         if (straddle) {
           asm volatile("" ::: "memory");
@@ -545,7 +611,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
         }
       }
     }
-    if (t + 1 < nt) {
+    if (more) {
       if (tid < C::BN) kpos_of(Next{})[tid] = key_live ? kpreg : kPosInf;
       wait_vmem();
     }
@@ -553,7 +619,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   };
 
   if (nt > 0) {
-    issue_tile(0, B0{});
+    issue_tile(0, B0{}, true);
     if (tid < C::BN) sKp0[tid] = key_live ? kpreg : kPosInf;
     wait_vmem();
   }

@@ -201,18 +201,13 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   const int32_t* pos_src = p.causal ? p.k_pos : (const int32_t*)p.k;
   typename C::Loader ld;
   ld.init(tid, kv_row_stride);
-  auto issue_tile = [&](int t, auto stage) {
+  auto issue_tile = [&](int t, auto stage, bool live) {
     const int j0 = (tb + t) * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
-    if (j0 + C::BN <= p.sk) {
-      ld.load(ktile(stage), kbase + o);
-      ld.load(vtile(stage), vbase + o);
-    } else {
-      ld.load_clamped(ktile(stage), kbase + o, kv_row_stride, p.sk - j0);
-      ld.load_clamped(vtile(stage), vbase + o, kv_row_stride, p.sk - j0);
-    }
-    pos_load_direct((lds_char*)(ptile(stage) + wave * C::BN), pos_src, j0,
-                    min(C::BN, p.sk - j0));
+    const int rows = uniform(live ? min(C::BN, p.sk - j0) : 0);
+    ld.load_clamped(ktile(stage), kbase + o, kv_row_stride, rows);
+    ld.load_clamped(vtile(stage), vbase + o, kv_row_stride, rows);
+    pos_load_direct((lds_char*)(ptile(stage) + wave * C::BN), pos_src, j0, rows);
   };
 
   f32x16 oacc[C::QB][C::MB];
@@ -238,7 +233,6 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     else if (t + 1 < nt) wait_vmem_le<C::VMEM>();
     else wait_vmem_le<0>();
     barrier_only();  // tile t visible to all waves; stage of tile t-1 free
-    if (t + 3 < nt) issue_tile(t + 3, Ahead{});
     const lds_char* kt = ktile(stage);
     const lds_char* vt = vtile(stage);
     const int* kp = ptile(stage) + wave * C::BN;
@@ -246,14 +240,18 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     const int klast = uniform(kp[C::BN - 1]);
     const int valid = min(C::BN, p.sk - (tb + t) * C::BN);
     const bool tail = valid < C::BN;
-    if (!wave_live || (causal && kfirst > wqmax) || klast < wqs_min) return;
+    // A wave whose rows cannot see the tile takes the masked path (all keys
+    // hidden, zero weights) instead of a branch, so that the next tiles'
+    // loads and the contractions below share one scheduling region.
+    const bool blind = !wave_live || (causal && kfirst > wqmax) || klast < wqs_min;
 
     f32x16 s[C::QB][C::NKB];
     // The two 32-key halves alternate, and the scheduling groups below keep
     // each K operand's LDS read four MFMAs ahead of its use (four reads, then
     // one after every MFMA).  Without them the first half's reads sat right
     // before their MFMAs, each waiting out the LDS latency.
-    auto scores = [&]() __attribute__((always_inline)) {
+    auto scores = [&](bool with_loads) __attribute__((always_inline)) {
+      if (with_loads) issue_tile(t + 3, Ahead{}, t + 3 < nt);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
@@ -268,9 +266,11 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
       for (int i = 0; i < C::KS * C::NKB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (with_loads && (i & 1) && i < 2 * C::VMEM)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     };
-    scores();
+    scores(true);
 
     uint32_t pk[C::QB][C::NKB][8];
     auto exps = [&](int qb, float neg_m, float& ps0, float& ps1) __attribute__((always_inline)) {
@@ -289,7 +289,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       // straddles this block's positions or sample starts
-      const bool straddle = tail || (causal && klast > bmin[qb]) || kfirst < bqs_max[qb];
+      const bool straddle =
+          blind || tail || (causal && klast > bmin[qb]) || kfirst < bqs_max[qb];
       // Unmasked tile of rows that all have a running max: exponentiate against
       // it directly.  A weight above 2^16 (a row max more than 16 above the
       // running one) sends the tile down the path that finds the tile max
@@ -301,7 +302,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
         if (__ballot(!(ps0 + ps1 <= 65536.0f))) {
           asm volatile("" ::: "memory");
           slow = true;
-          scores();
+          scores(false);
         }
       }
       if (slow) {
@@ -368,9 +369,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     }
   };
 
-  if (nt > 0) issue_tile(0, S0{});
-  if (nt > 1) issue_tile(1, S1{});
-  if (nt > 2) issue_tile(2, S2{});
+  if (nt > 0) issue_tile(0, S0{}, true);
+  issue_tile(1, S1{}, nt > 1);
+  issue_tile(2, S2{}, nt > 2);
   for (int t = 0; t < nt; t += 4) {
     step(S0{}, t);
     if (t + 1 < nt) step(S1{}, t + 1);

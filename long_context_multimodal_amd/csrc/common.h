@@ -126,14 +126,15 @@ __device__ __forceinline__ int tile_off(int row, int c) {
 }
 
 // Buffer resource over [base, base + nbytes) (raw, stride 0; gfx9 dword 3 =
-// 32-bit data format).  The base is taken from lane 0: callers pass
-// wave-uniform addresses, and reading it through readfirstlane keeps the
+// 32-bit data format).  Base and size are taken from lane 0: callers pass
+// wave-uniform values, and reading them through readfirstlane keeps the
 // descriptor in scalar registers without a waterfall loop.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t nbytes) {
   const uint64_t a = (uint64_t)base;
   const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)u, (short)0, (int)nbytes, 0x00020000);
+  const int n = __builtin_amdgcn_readfirstlane((int)nbytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)u, (short)0, n, 0x00020000);
 }
 
 __device__ __forceinline__ uint32_t clamp_bytes(size_t n) {

@@ -76,9 +76,13 @@ def test_ring_with_alternating_tile_blocks(mm, packed):
     assert_close_rms(to_np(dq), ref["dq"], bound=ref["mq"], what="dQ")
 
 
-def _chain_vs_oracle(mm, qp, kp, hq, hkv, d, seed):
+def _chain_vs_oracle(mm, qp, kp, hq, hkv, d, seed, kv_loose=False):
     """GPU forward -> bf16 O -> preprocess -> backward of one chunk, every
-    element against the oracle (delta from the oracle's own O)."""
+    element against the oracle (delta from the oracle's own O).  With
+    ``kv_loose`` the absolute bounds are dropped for dK and dV: when a key is
+    seen by tens of thousands of rows its gradients are of order one, and the
+    RMS-relative mean and the elementwise rounding bound are the checks that
+    scale with them."""
     mmsp, _ = mm
     import torch
     sq, sk = len(qp), len(kp)
@@ -97,8 +101,9 @@ def _chain_vs_oracle(mm, qp, kp, hq, hkv, d, seed):
     assert_close_abs(to_np(o), ref["o"], what="O")
     assert_close_abs(to_np(lse), ref["lse"], what="LSE")
     assert_close_rms(to_np(dq), ref["dq"], bound=ref["mq"], what="dQ")
-    assert_close_rms(to_np(dk), ref["dk"][0], bound=ref["mk"][0], what="dK")
-    assert_close_rms(to_np(dv), ref["dv"][0], bound=ref["mv"][0], what="dV")
+    loose = dict(max_abs=np.inf, mean_abs=np.inf) if kv_loose else {}
+    assert_close_rms(to_np(dk), ref["dk"][0], bound=ref["mk"][0], what="dK", **loose)
+    assert_close_rms(to_np(dv), ref["dv"][0], bound=ref["mv"][0], what="dV", **loose)
 
 
 def test_dkdv_tiling_of_the_2m_share(mm):
@@ -112,7 +117,8 @@ def test_dkdv_tiling_of_the_2m_share(mm):
 
 def test_dq_and_forward_tiling_of_the_2m_share(mm):
     """65,536 queries x 4 heads (dQ: 512 query tiles per head on a grid of
-    2048; forward: 256 on 1024) against 512 keys at positions 128 j."""
+    2048; forward: 256 on 1024) against 512 keys at positions 128 j (key j
+    is seen by 65,536 - 128 j rows, so dK and dV reach order one)."""
     qp = np.arange(65536, dtype=np.int32)
     kp = (np.arange(512) * 128).astype(np.int32)
-    _chain_vs_oracle(mm, qp, kp, 4, 4, 128, seed=410)
+    _chain_vs_oracle(mm, qp, kp, 4, 4, 128, seed=410, kv_loose=True)
