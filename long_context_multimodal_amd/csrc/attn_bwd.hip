@@ -196,14 +196,31 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     nx_q0 = wrap ? qt0 * C::BQ : nx_q0 + C::BQ;
     nx_h = wrap ? nx_h + 1 : nx_h;
     nx_off = wrap ? nx_off + tile_step - head_back : nx_off + tile_step;
-    const int rows = uniform(live ? min(C::BQ, p.sq - q0) : 0);
-    ld.load_clamped(qtile(buf), p.q + o, q_row_stride, rows);
-    ld.load_clamped(otile(buf), p.dout + o, q_row_stride, rows);
-    // Raw values only: they are converted when published, after the wait
+    // Raw statistics only: they are converted when published, after the wait
     // that ends the step, so no load here is waited for inside the step.
     const int i = min(q0 + min(lane, C::BQ - 1), p.sq - 1);
-    stat = stat_src[(size_t)h * stat_head + i];
-    row_live = q0 + lane < p.sq;
+    if constexpr (packed) {
+      // packed samples issue these at the top of the step (many short
+      // workgroups), where the plain branches cost less than the clamped forms
+      if (!live) return;
+      if (q0 + C::BQ <= p.sq) {
+        ld.load(qtile(buf), p.q + o);
+        ld.load(otile(buf), p.dout + o);
+      } else {
+        ld.load_clamped(qtile(buf), p.q + o, q_row_stride, p.sq - q0);
+        ld.load_clamped(otile(buf), p.dout + o, q_row_stride, p.sq - q0);
+      }
+      if (lane <= C::BQ) {
+        stat = stat_src[(size_t)h * stat_head + i];
+        row_live = q0 + lane < p.sq;
+      }
+    } else {
+      const int rows = uniform(live ? min(C::BQ, p.sq - q0) : 0);
+      ld.load_clamped(qtile(buf), p.q + o, q_row_stride, rows);
+      ld.load_clamped(otile(buf), p.dout + o, q_row_stride, rows);
+      stat = stat_src[(size_t)h * stat_head + i];
+      row_live = q0 + lane < p.sq;
+    }
   };
   // Each wave converts its statistic and writes it with one store: the
   // destination row is fixed per wave, so only the lane offset is a register.
@@ -241,13 +258,19 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     const lds_char* qt = qtile(buf_tag);
     const lds_char* dt = otile(buf_tag);
     const int qfirst = uniform(sQp(BUF)[0]);
+    const int qlast = uniform(sQp(BUF)[C::BQ]);
+    const int qs_first = packed ? uniform(sQs(BUF)[0]) : INT_MIN;
     const int qs_last = packed ? uniform(sQs(BUF)[C::BQ - 1]) : INT_MIN;
     // Every wave runs every tile: one whose keys the tile's rows cannot see
     // (only next to the causal diagonal) masks all its scores and adds zeros.
     // Without a branch here, the next tile's loads share one scheduling
-    // region with the contractions below.
-    {
-      issue_next(Next{}, more);
+    // region with the contractions below.  Packed samples issue the loads
+    // first and skip such tiles: there a wave's keys often belong to another
+    // sample than the tile's rows.
+    const bool sees = wave_live && qlast >= wkmin && qs_first <= wkmax;
+    if constexpr (packed) issue_next(Next{}, more);
+    if (!packed || sees) {
+      if constexpr (!packed) issue_next(Next{}, more);
       // S = Q K^T and dP = dO V^T  (row = query, col = key)
       f32x16 s = mfma32x32x16(lds_read_b128(qt, qoff[0]), kf[0], f32x16{});
       f32x16 dp = mfma32x32x16(lds_read_b128(dt, qoff[0]), lds_read_b128(vrows, qoff[0]),
@@ -344,9 +367,34 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   // Each wave instead passes its 32 keys through LDS (free after the loop's
   // last barrier) and writes whole rows: a store of 64 lanes x 16 bytes covers
   // 1 KiB of consecutive rows.  The accumulator's 16-byte pieces are dumped
-  // as they are, one 1 KiB block per (32-column block, 8-row group) with lane
-  // L's piece in slot L ^ block, so the dump is a plain 1 KiB write and the
-  // 32 lanes that later read one row's pieces hit 16 different bank groups.
+  // as they are, one 1 KiB block b per (32-column block, 8-row group), lane
+  // L = 32 hh + r's piece in slot L ^ b ^ 8 hh: each dump is a 1 KiB write
+  // whose 16-lane groups cover 16 bank groups, and so are the 16-lane groups
+  // that read back one row's pieces (blocks b = 0..7 of both halves hh).
+  if constexpr (PACKED) {
+    // Packed samples make many short workgroups, which the LDS pass below
+    // costs ~2% of their time; they store the 16-byte pieces directly.
+    if (!key_ok) return;
+    float* dkr = p.dk + (size_t)key * kv_stride + (size_t)kvh * D;
+    float* dvr = p.dv + (size_t)key * kv_stride + (size_t)kvh * D;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = mb * 32 + 8 * g + 4 * hh;
+        f32x4 kv4 = {dkacc[mb][4 * g] * p.scale, dkacc[mb][4 * g + 1] * p.scale,
+                     dkacc[mb][4 * g + 2] * p.scale, dkacc[mb][4 * g + 3] * p.scale};
+        f32x4 vv4 = {dvacc[mb][4 * g], dvacc[mb][4 * g + 1], dvacc[mb][4 * g + 2],
+                     dvacc[mb][4 * g + 3]};
+        if (p.accumulate) {
+          kv4 += *(const f32x4*)(dkr + d0);
+          vv4 += *(const f32x4*)(dvr + d0);
+        }
+        *(f32x4*)(dkr + d0) = kv4;
+        *(f32x4*)(dvr + d0) = vv4;
+      }
+    return;
+  }
   if (!wave_live) return;
   constexpr int NB = C::MB * 4;          // 1 KiB blocks per accumulator
   constexpr int CH = D / 4;              // 16-byte pieces per fp32 row
@@ -379,15 +427,15 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
         lds_char* blk = (b < NB / 2 ? reg0 + b * 1024 : reg1 + (b - NB / 2) * 1024);
         const f32x4 v4 = {acc[mb][4 * g] * mul, acc[mb][4 * g + 1] * mul,
                           acc[mb][4 * g + 2] * mul, acc[mb][4 * g + 3] * mul};
-        *(__attribute__((address_space(3))) f32x4*)(blk + ((lane ^ b) << 4)) = v4;
+        *(__attribute__((address_space(3))) f32x4*)(blk + ((lane ^ b ^ (hh << 3)) << 4)) = v4;
       }
     wait_lds_writes();
 #pragma unroll
     for (int i = 0; i < READS; ++i) {
       const int rr = (i * kWave + lane) / CH;
       const int slot = ((cc & 1) << 5) | rr;
-      const f32x4 v4 =
-          *(const __attribute__((address_space(3))) f32x4*)(rbase + ((slot ^ rb) << 4));
+      const f32x4 v4 = *(const __attribute__((address_space(3))) f32x4*)(
+          rbase + ((slot ^ rb ^ ((cc & 1) << 3)) << 4));
       const int k = wk0 + rr;
       if (k < p.sk) {
         float* dst = out + (size_t)k * kv_stride + (size_t)kvh * D + cc * 4;
@@ -532,12 +580,27 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   auto issue_tile = [&](int t, auto buf, bool live) {
     const int j0 = (tb + t) * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
-    const int rows = uniform(live ? min(C::BN, p.sk - j0) : 0);
-    ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, rows);
-    ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, rows);
-    // raw position; keys past sk are hidden when published
-    kpreg = p.causal ? p.k_pos[max(0, min(j0 + (tid & (C::BN - 1)), p.sk - 1))] : 0;
-    key_live = j0 + (tid & (C::BN - 1)) < p.sk;
+    if constexpr (packed) {  // at the top of the step, plain branches (see dK/dV)
+      if (!live) return;
+      if (j0 + C::BN <= p.sk) {
+        ld.load(ktile(buf), kbase + o);
+        ld.load(vtile(buf), vbase + o);
+      } else {
+        ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, p.sk - j0);
+        ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, p.sk - j0);
+      }
+      if (tid < C::BN) {  // raw position; keys past sk are hidden when published
+        kpreg = p.causal ? p.k_pos[min(j0 + tid, p.sk - 1)] : 0;
+        key_live = j0 + tid < p.sk;
+      }
+    } else {
+      const int rows = uniform(live ? min(C::BN, p.sk - j0) : 0);
+      ld.load_clamped(ktile(buf), kbase + o, kv_row_stride, rows);
+      ld.load_clamped(vtile(buf), vbase + o, kv_row_stride, rows);
+      // raw position; keys past sk are hidden when published
+      kpreg = p.causal ? p.k_pos[max(0, min(j0 + (tid & (C::BN - 1)), p.sk - 1))] : 0;
+      key_live = j0 + (tid & (C::BN - 1)) < p.sk;
+    }
   };
 
   f32x16 dqacc[C::MB];
@@ -556,14 +619,17 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
     const int klast = uniform(kp[C::BN - 1]);
     // Every wave runs every tile: one whose rows cannot see it (only next to
     // the causal diagonal, or rows past sq) takes the masked path, which
-    // hides all its keys, and adds zeros.
-    {
+    // hides all its keys, and adds zeros.  Packed samples issue the loads
+    // first and skip such tiles (see the dK/dV kernel).
+    const bool sees = wave_live && kfirst <= wqmax && klast >= wqs_min;
+    if constexpr (packed) issue_tile(t + 1, Next{}, more);
+    if (!packed || sees) {
       // straddles the rows' positions or their sample starts
       const bool straddle = !wave_live || klast > wqmin || kfirst < wqs_max;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {  // 32 keys at a time
         const int rb = kb * 32 * D * 2;
-        if (kb == 0) issue_tile(t + 1, Next{}, more);
+        if (!packed && kb == 0) issue_tile(t + 1, Next{}, more);
         f32x16 s = mfma32x32x16(lds_read_b128(kt, rb + koff[0]), qf[0], f32x16{});
         f32x16 dp = mfma32x32x16(lds_read_b128(vt, rb + koff[0]), df[0], f32x16{});
 #pragma unroll

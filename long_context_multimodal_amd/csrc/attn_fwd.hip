@@ -242,8 +242,15 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     const bool tail = valid < C::BN;
     // A wave whose rows cannot see the tile takes the masked path (all keys
     // hidden, zero weights) instead of a branch, so that the next tiles'
-    // loads and the contractions below share one scheduling region.
+    // loads and the contractions below share one scheduling region.  Packed
+    // samples are the exception: there whole waves often belong to another
+    // sample than the tile, and skipping leaves the matrix core to the other
+    // wave on the SIMD, so they issue the loads first and leave the step.
     const bool blind = !wave_live || (causal && kfirst > wqmax) || klast < wqs_min;
+    if constexpr (PACKED) {
+      issue_tile(t + 3, Ahead{}, t + 3 < nt);
+      if (blind) return;
+    }
 
     f32x16 s[C::QB][C::NKB];
     // The two 32-key halves alternate, and the scheduling groups below keep
@@ -270,7 +277,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     };
-    scores(true);
+    scores(!PACKED);
 
     uint32_t pk[C::QB][C::NKB][8];
     auto exps = [&](int qb, float neg_m, float& ps0, float& ps1) __attribute__((always_inline)) {
