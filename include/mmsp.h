@@ -49,6 +49,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The HIP runtime's stream handle (the same declaration as hip_runtime_api.h,
+ * so this header needs no HIP include and agrees with it when both are seen). */
+typedef struct ihipStream_t* hipStream_t;
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -104,7 +108,7 @@ size_t mmsp_shard_balance_workspace_bytes(int64_t n, int32_t n_ranks, int32_t mo
                                           int32_t granularity);
 int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
                        int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
-                       void* d_workspace, size_t workspace_bytes, void* stream);
+                       void* d_workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---- a1 without allocation ---------------------------------------------------
  * For callers that cannot allocate device memory or hand over a workspace
@@ -124,7 +128,7 @@ int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int3
 #define MMSP_NOALLOC_MAX_BLOCKS 65536
 int mmsp_shard_balance_noalloc(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
                                int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
-                               void* stream);
+                               hipStream_t stream);
 
 /* ---- a1 for packed samples: per-sample zigzag ------------------------------
  * Variable-length videos packed into one buffer with reset attention masks
@@ -152,7 +156,7 @@ int mmsp_shard_balance_noalloc(const uint8_t* d_labels, int64_t n, int32_t n_ran
  */
 int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_t n,
                               int32_t n_ranks, int32_t* d_perm, int32_t* d_inv_perm,
-                              int32_t* d_token_start, void* stream);
+                              int32_t* d_token_start, hipStream_t stream);
 
 /* ---- precondition check of positions ----------------------------------------
  * The attention calls take position arrays as strictly increasing and packed
@@ -166,7 +170,7 @@ int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_
  * before every attention call when MMSP_CHECK_POSITIONS=1.
  */
 int mmsp_check_positions(const int32_t* d_pos, const int32_t* d_starts, int32_t n,
-                         int32_t* d_violations, void* stream);
+                         int32_t* d_violations, hipStream_t stream);
 
 /* ---- a1: token rows into shard order, and back -----------------------------
  * Each rank holds N/P tokens of the stream ("LongVILA Guide ...", section
@@ -184,9 +188,9 @@ int mmsp_check_positions(const int32_t* d_pos, const int32_t* d_starts, int32_t 
  * memory-bound.
  */
 int mmsp_shard_gather(const void* d_src, int64_t src_rows, const int32_t* d_rows, int64_t n_rows,
-                      int64_t row_bytes, void* d_dst, void* stream);
+                      int64_t row_bytes, void* d_dst, hipStream_t stream);
 int mmsp_shard_scatter(const void* d_src, int64_t n_rows, const int32_t* d_rows,
-                       int64_t dst_rows, int64_t row_bytes, void* d_dst, void* stream);
+                       int64_t dst_rows, int64_t row_bytes, void* d_dst, hipStream_t stream);
 
 /* ---- a2: attention of the query shard against one KV chunk ---------------
  * Source: "LongVILA Guide ...", sections "Multi-Modal Sequence Parallelism
@@ -215,7 +219,7 @@ enum { MMSP_CAUSAL = 1u, MMSP_ACCUMULATE = 2u };
 int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32_t* q_pos,
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* o, float* lse,
-                        void* stream);
+                        hipStream_t stream);
 
 /* ---- a2 with packed samples -------------------------------------------------
  * As mmsp_attn_fwd_chunk, with reset attention masks between packed samples
@@ -230,7 +234,7 @@ int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
                                const int32_t* q_pos, const int32_t* q_start,
                                const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
                                int32_t hkv, int32_t d, float scale, uint32_t flags, float* o,
-                               float* lse, void* stream);
+                               float* lse, hipStream_t stream);
 
 /* ---- a3: log-sum-exp merge of two chunk results ---------------------------
  * The page's ring loop ("Implementation ...") adds each step's output into an
@@ -245,7 +249,7 @@ int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
  *   (round-to-nearest-even).  d in {64, 128}.
  */
 int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
-                   int32_t sq, int32_t hq, int32_t d, void* o_final_bf16, void* stream);
+                   int32_t sq, int32_t hq, int32_t d, void* o_final_bf16, hipStream_t stream);
 
 /* ---- a5: backward preprocess ----------------------------------------------
  * delta[h][i] = sum_c dout[i][h][c] * o[i][h][c] (fp32 accumulation) from the
@@ -254,7 +258,7 @@ int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const floa
  * be the dq_acc of the following mmsp_attn_bwd_chunk calls.
  */
 int mmsp_attn_bwd_preprocess(const void* o, const void* dout, int32_t sq, int32_t hq, int32_t d,
-                             float* delta, float* dq_zero, void* stream);
+                             float* delta, float* dq_zero, hipStream_t stream);
 
 /* ---- a6: backward of one chunk from the saved final LSE --------------------
  * Training without gradient checkpointing ("LongVILA - ... (Jason's Study)",
@@ -282,7 +286,7 @@ int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void*
                         const float* lse, const float* delta, const int32_t* q_pos,
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* dq_acc, float* dk,
-                        float* dv, void* stream);
+                        float* dv, hipStream_t stream);
 
 /* ---- a6 with packed samples -------------------------------------------------
  * As mmsp_attn_bwd_chunk with the packed-sample visibility of
@@ -294,7 +298,7 @@ int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, cons
                                const int32_t* q_start, const int32_t* k_pos, int32_t sq,
                                int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
                                uint32_t flags, float* dq_acc, float* dk, float* dv,
-                               void* stream);
+                               hipStream_t stream);
 
 /* ---- a4: one rank's ring loop over resident chunks -----------------------
  * "LongVILA Guide ...", section "Implementation: PyTorch Distributed
@@ -333,14 +337,14 @@ int mmsp_ring_forward(const void* q, const void* const* k_chunks, const void* co
                       const int32_t* q_pos, const int32_t* const* k_pos_chunks,
                       const int32_t* q_start, int32_t n_chunks, int32_t rank, int32_t sq,
                       int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
-                      uint32_t flags, float* o, float* lse, void* o_final_bf16, void* stream);
+                      uint32_t flags, float* o, float* lse, void* o_final_bf16, hipStream_t stream);
 int mmsp_ring_backward(const void* q, const void* const* k_chunks, const void* const* v_chunks,
                        const void* dout, const void* o_bf16, const float* lse,
                        const int32_t* q_pos, const int32_t* const* k_pos_chunks,
                        const int32_t* q_start, int32_t n_chunks, int32_t rank, int32_t sq,
                        int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
                        uint32_t flags, float* delta, float* dq, float* const* dk_chunks,
-                       float* const* dv_chunks, void* stream);
+                       float* const* dv_chunks, hipStream_t stream);
 
 /* ---- rotary position embedding at global positions ------------------------
  * "LongVILA Guide ...", section "Three-Stage Long-Context Alignment
@@ -365,7 +369,7 @@ int mmsp_ring_backward(const void* q, const void* const* k_chunks, const void* c
 enum { MMSP_DTYPE_BF16 = 0, MMSP_DTYPE_F32 = 1 };
 
 int mmsp_rope(const void* x, void* y, int32_t dtype, const int32_t* pos, int32_t s, int32_t h,
-              int32_t d, double theta, int32_t inverse, void* stream);
+              int32_t d, double theta, int32_t inverse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ inline bool bad_dim(int32_t d) { return d != 64 && d != 128; }
 
 inline int check_hip(hipError_t e) { return e == hipSuccess ? MMSP_OK : MMSP_ERR_HIP; }
 
-inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline hipStream_t as_stream(hipStream_t s) { return s; }
 
 int check_attn_shapes(int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale) {
   if (sq <= 0 || sk <= 0 || hq <= 0 || hkv <= 0) return MMSP_ERR_SHAPE;
@@ -38,7 +38,7 @@ namespace {
 int attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_pos,
              const int32_t* q_start, const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
              int32_t hkv, int32_t d, float scale, uint32_t flags, float* o, float* lse,
-             void* stream) {
+             hipStream_t stream) {
   if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
   const bool causal = (flags & MMSP_CAUSAL) != 0;
   if (!q || !k || !v || !o || !lse) return MMSP_ERR_NULL;
@@ -70,7 +70,7 @@ int attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_pos,
 int attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse,
              const float* delta, const int32_t* q_pos, const int32_t* q_start,
              const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d,
-             float scale, uint32_t flags, float* dq_acc, float* dk, float* dv, void* stream) {
+             float scale, uint32_t flags, float* dq_acc, float* dk, float* dv, hipStream_t stream) {
   if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE | MMSP_BWD_NO_DQ | MMSP_BWD_NO_DKDV)) !=
       0)
     return MMSP_ERR_UNSUPPORTED;
@@ -175,7 +175,7 @@ int check_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t m
 
 int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
                        int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
-                       void* d_workspace, size_t workspace_bytes, void* stream) {
+                       void* d_workspace, size_t workspace_bytes, hipStream_t stream) {
   const int st = check_balance(d_labels, n, n_ranks, mode, granularity, d_perm);
   if (st != MMSP_OK) return st;
   int32_t* ws_vis = nullptr;
@@ -193,7 +193,7 @@ int mmsp_shard_balance(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int3
 
 int mmsp_shard_balance_noalloc(const uint8_t* d_labels, int64_t n, int32_t n_ranks, int32_t mode,
                                int32_t granularity, int32_t* d_perm, int32_t* d_inv_perm,
-                               void* stream) {
+                               hipStream_t stream) {
   const int st = check_balance(d_labels, n, n_ranks, mode, granularity, d_perm);
   if (st != MMSP_OK) return st;
   int32_t* ws_vis = nullptr;
@@ -209,7 +209,7 @@ int mmsp_shard_balance_noalloc(const uint8_t* d_labels, int64_t n, int32_t n_ran
 
 int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_t n,
                               int32_t n_ranks, int32_t* d_perm, int32_t* d_inv_perm,
-                              int32_t* d_token_start, void* stream) {
+                              int32_t* d_token_start, hipStream_t stream) {
   if (!d_starts || !d_perm) return MMSP_ERR_NULL;
   if (n <= 0 || n > kMaxElems || n_ranks <= 0 || n_ranks > kMaxRanks || n_samples <= 0 ||
       n_samples > n)
@@ -222,7 +222,7 @@ int mmsp_shard_balance_packed(const int32_t* d_starts, int32_t n_samples, int64_
 
 namespace {
 int move_rows(const void* src, const int32_t* rows, int64_t n_rows, int64_t indexed_rows,
-              int64_t row_bytes, void* dst, bool gather, void* stream) {
+              int64_t row_bytes, void* dst, bool gather, hipStream_t stream) {
   if (!src || !rows || !dst) return MMSP_ERR_NULL;
   if (n_rows <= 0 || indexed_rows <= 0 || n_rows > kMaxElems || indexed_rows > kMaxElems ||
       row_bytes < 16 || row_bytes % 16 != 0 || row_bytes / 16 > kMaxElems)
@@ -233,7 +233,7 @@ int move_rows(const void* src, const int32_t* rows, int64_t n_rows, int64_t inde
 }  // namespace
 
 int mmsp_check_positions(const int32_t* d_pos, const int32_t* d_starts, int32_t n,
-                         int32_t* d_violations, void* stream) {
+                         int32_t* d_violations, hipStream_t stream) {
   if (!d_pos || !d_violations) return MMSP_ERR_NULL;
   if (n <= 0) return MMSP_ERR_SHAPE;
   return check_hip(mmsp::launch_check_positions(d_pos, d_starts, n, d_violations,
@@ -241,19 +241,19 @@ int mmsp_check_positions(const int32_t* d_pos, const int32_t* d_starts, int32_t 
 }
 
 int mmsp_shard_gather(const void* d_src, int64_t src_rows, const int32_t* d_rows, int64_t n_rows,
-                      int64_t row_bytes, void* d_dst, void* stream) {
+                      int64_t row_bytes, void* d_dst, hipStream_t stream) {
   return move_rows(d_src, d_rows, n_rows, src_rows, row_bytes, d_dst, true, stream);
 }
 
 int mmsp_shard_scatter(const void* d_src, int64_t n_rows, const int32_t* d_rows,
-                       int64_t dst_rows, int64_t row_bytes, void* d_dst, void* stream) {
+                       int64_t dst_rows, int64_t row_bytes, void* d_dst, hipStream_t stream) {
   return move_rows(d_src, d_rows, n_rows, dst_rows, row_bytes, d_dst, false, stream);
 }
 
 int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32_t* q_pos,
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* o, float* lse,
-                        void* stream) {
+                        hipStream_t stream) {
   return attn_fwd(q, k, v, q_pos, nullptr, k_pos, sq, sk, hq, hkv, d, scale, flags, o, lse,
                   stream);
 }
@@ -262,7 +262,7 @@ int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
                                const int32_t* q_pos, const int32_t* q_start,
                                const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
                                int32_t hkv, int32_t d, float scale, uint32_t flags, float* o,
-                               float* lse, void* stream) {
+                               float* lse, hipStream_t stream) {
   if (!(flags & MMSP_CAUSAL)) return MMSP_ERR_UNSUPPORTED;
   if (!q_start) return MMSP_ERR_NULL;
   return attn_fwd(q, k, v, q_pos, q_start, k_pos, sq, sk, hq, hkv, d, scale, flags, o, lse,
@@ -270,7 +270,7 @@ int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
 }
 
 int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
-                   int32_t sq, int32_t hq, int32_t d, void* o_final_bf16, void* stream) {
+                   int32_t sq, int32_t hq, int32_t d, void* o_final_bf16, hipStream_t stream) {
   if (!o_acc || !lse_acc) return MMSP_ERR_NULL;
   if ((o_part == nullptr) != (lse_part == nullptr)) return MMSP_ERR_NULL;
   if (sq <= 0 || hq <= 0) return MMSP_ERR_SHAPE;
@@ -283,7 +283,7 @@ int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const floa
 }
 
 int mmsp_attn_bwd_preprocess(const void* o, const void* dout, int32_t sq, int32_t hq, int32_t d,
-                             float* delta, float* dq_zero, void* stream) {
+                             float* delta, float* dq_zero, hipStream_t stream) {
   if (!o || !dout || !delta) return MMSP_ERR_NULL;
   if (sq <= 0 || hq <= 0) return MMSP_ERR_SHAPE;
   if (bad_dim(d)) return MMSP_ERR_UNSUPPORTED;
@@ -297,7 +297,7 @@ int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void*
                         const float* lse, const float* delta, const int32_t* q_pos,
                         const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv,
                         int32_t d, float scale, uint32_t flags, float* dq_acc, float* dk,
-                        float* dv, void* stream) {
+                        float* dv, hipStream_t stream) {
   return attn_bwd(q, k, v, dout, lse, delta, q_pos, nullptr, k_pos, sq, sk, hq, hkv, d, scale,
                   flags, dq_acc, dk, dv, stream);
 }
@@ -307,7 +307,7 @@ int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, cons
                                const int32_t* q_start, const int32_t* k_pos, int32_t sq,
                                int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
                                uint32_t flags, float* dq_acc, float* dk, float* dv,
-                               void* stream) {
+                               hipStream_t stream) {
   if (!(flags & MMSP_CAUSAL)) return MMSP_ERR_UNSUPPORTED;
   if (!q_start) return MMSP_ERR_NULL;
   return attn_bwd(q, k, v, dout, lse, delta, q_pos, q_start, k_pos, sq, sk, hq, hkv, d, scale,
@@ -320,7 +320,7 @@ int mmsp_ring_forward(const void* q, const void* const* k_chunks, const void* co
                       const int32_t* q_pos, const int32_t* const* k_pos_chunks,
                       const int32_t* q_start, int32_t n_chunks, int32_t rank, int32_t sq,
                       int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
-                      uint32_t flags, float* o, float* lse, void* o_final_bf16, void* stream) {
+                      uint32_t flags, float* o, float* lse, void* o_final_bf16, hipStream_t stream) {
   if ((flags & ~(uint32_t)MMSP_CAUSAL) != 0) return MMSP_ERR_UNSUPPORTED;
   const bool causal = (flags & MMSP_CAUSAL) != 0;
   if (q_start && !causal) return MMSP_ERR_UNSUPPORTED;
@@ -350,7 +350,7 @@ int mmsp_ring_backward(const void* q, const void* const* k_chunks, const void* c
                        const int32_t* q_start, int32_t n_chunks, int32_t rank, int32_t sq,
                        int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
                        uint32_t flags, float* delta, float* dq, float* const* dk_chunks,
-                       float* const* dv_chunks, void* stream) {
+                       float* const* dv_chunks, hipStream_t stream) {
   if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
   const bool causal = (flags & MMSP_CAUSAL) != 0;
   if (q_start && !causal) return MMSP_ERR_UNSUPPORTED;
@@ -380,7 +380,7 @@ int mmsp_ring_backward(const void* q, const void* const* k_chunks, const void* c
 }
 
 int mmsp_rope(const void* x, void* y, int32_t dtype, const int32_t* pos, int32_t s, int32_t h,
-              int32_t d, double theta, int32_t inverse, void* stream) {
+              int32_t d, double theta, int32_t inverse, hipStream_t stream) {
   if (!x || !y || !pos) return MMSP_ERR_NULL;
   if (dtype != MMSP_DTYPE_BF16 && dtype != MMSP_DTYPE_F32) return MMSP_ERR_UNSUPPORTED;
   if (inverse != 0 && inverse != 1) return MMSP_ERR_UNSUPPORTED;

@@ -300,3 +300,28 @@ def test_shard_balance_noalloc_rejects():
     assert f(FAKE, 1000, 4, 1, 16, FAKE, None, None) == -4      # not a multiple of 2*P*g
     # past the static scratch: 131,072 blocks of 16 tokens
     assert f(FAKE, 1 << 21, 8, 1, 16, FAKE, None, None) == -5
+
+
+def test_header_compiles_as_c(tmp_path):
+    """include/mmsp.h is a C header: it compiles as C99 on its own, and as C11
+    next to the HIP runtime's header (both declare the same hipStream_t)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "use.c"
+    src.write_text('#include "mmsp.h"\n'
+                   "int main(void) { hipStream_t s = 0;\n"
+                   "  return mmsp_lse_merge(0, 0, 0, 0, 1, 1, 64, 0, s) == MMSP_ERR_NULL ? 0 : 1; }\n")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c",
+                        str(src), "-o", str(tmp_path / "use.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    hip_inc = "/opt/rocm/include"
+    if os.path.exists(os.path.join(hip_inc, "hip", "hip_runtime_api.h")):
+        src2 = tmp_path / "use_hip.c"
+        src2.write_text("#include <hip/hip_runtime_api.h>\n" + src.read_text())
+        r = subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                            "-I", hip_inc, "-I", os.path.dirname(HEADER), "-c", str(src2), "-o",
+                            str(tmp_path / "use_hip.o")], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
