@@ -13,10 +13,19 @@
 //  * each wave owns 32 query rows; Q stays in registers; the 8 waves share
 //    every K/V tile, so each tile crosses HBM/L2 -> LDS once per 256 rows;
 //  * K/V tiles of 64 keys go straight from HBM to a 4-stage, XOR-swizzled
-//    LDS ring with 16-byte direct loads (no staging registers), three tiles
-//    in flight ahead of the one being used; each stage
-//    is its own LDS object so loads into one never stall reads of another;
-//    the key positions of a tile are loaded directly into a per-wave slot;
+//    LDS ring with 16-byte direct loads (no staging registers); each stage
+//    is one LDS object holding the K tile, the V tile and the tile's key
+//    positions (one slot per wave), so the compiler tracks the loads into
+//    one stage apart from reads of the others; rows past the chunk's end
+//    lie outside the load's buffer range and arrive as zeros;
+//  * the two waves on a SIMD (waves w and w + 4) run half a tile apart:
+//    group 1 (waves 4-7) runs the same program one barrier behind group 0,
+//    so while one wave runs its contractions (P V of tile t, then the
+//    scores of tile t + 1, 32 MFMAs) the other runs the softmax of its
+//    tile, and the matrix core and the vector ALU work at the same time.
+//    The contracting wave raises its priority so the softmax beside it does
+//    not hold back its MFMA issue.  Loads run two tiles ahead (a stage is
+//    free once both groups finished P V of its tile);
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a lane holds 16 scores of ONE
 //    query, so the row max/sum are in-lane plus one permlane32 swap;
 //  * O^T += V^T P^T: the score registers, converted to bf16, are the B
@@ -28,9 +37,9 @@
 //    on unmasked tiles of rows that already have a running max the tile max
 //    is not even computed: weights are taken against the running max, and a
 //    lane row sum above 2^16 (a row max more than 16 above it) sends the
-//    tile back through the max-and-rescale path, its scores recomputed from
-//    the K tile still in LDS; row sums stay in fp32 (exact LSE for the
-//    merge and the backward);
+//    tile back through the max-and-rescale path (the scores are still in
+//    registers; the packed path recomputes them from the K tile in LDS);
+//    row sums stay in fp32 (exact LSE for the merge and the backward);
 //  * causal tile skipping from the sorted positions: a binary search bounds
 //    the key range of the workgroup, each wave skips tiles it cannot see and
 //    masks only the tiles that straddle its rows' positions (or the tail),
@@ -39,7 +48,9 @@
 //  * packed samples (reset masks between samples packed in one buffer) take
 //    a per-query sample start that also bounds the key range from below;
 //    they run in their own template instance, so the plain path has none of
-//    that code;
+//    that code.  There all 8 waves step through the tiles together, three
+//    tiles in flight, and a wave whose rows belong to other samples skips
+//    the tile's contractions;
 //  * GQA: query head h reads KV head h / G; the workgroup order keeps the
 //    query heads of one KV head on one XCD (shared L2) and dispatches the
 //    heavier (causally longer) query tiles first; when one head's tiles span
@@ -72,35 +83,21 @@ struct FwdCfg {
 template <int D, bool ACC, bool PACKED>
 __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  // one LDS object per pipeline stage
+  // one LDS object per pipeline stage: K tile, V tile, then the key
+  // positions of the tile (one 64-entry slot per wave)
   static_assert(C::NS == 4, "stage objects below are written out for four stages");
-  __shared__ __attribute__((aligned(16))) char sK0[C::TILE], sK1[C::TILE], sK2[C::TILE],
-      sK3[C::TILE];
-  __shared__ __attribute__((aligned(16))) char sV0[C::TILE], sV1[C::TILE], sV2[C::TILE],
-      sV3[C::TILE];
-  __shared__ __attribute__((aligned(16))) int sP0[C::WAVES * C::BN], sP1[C::WAVES * C::BN],
-      sP2[C::WAVES * C::BN], sP3[C::WAVES * C::BN];
-  auto ktile = [&](auto b) -> lds_char* {
+  constexpr int STAGE = 2 * C::TILE + C::WAVES * C::BN * 4;
+  __shared__ __attribute__((aligned(16))) char sS0[STAGE], sS1[STAGE], sS2[STAGE], sS3[STAGE];
+  auto stage_base = [&](auto b) -> lds_char* {
     constexpr int S = decltype(b)::value;
-    if constexpr (S == 0) return (lds_char*)sK0;
-    else if constexpr (S == 1) return (lds_char*)sK1;
-    else if constexpr (S == 2) return (lds_char*)sK2;
-    else return (lds_char*)sK3;
+    if constexpr (S == 0) return (lds_char*)sS0;
+    else if constexpr (S == 1) return (lds_char*)sS1;
+    else if constexpr (S == 2) return (lds_char*)sS2;
+    else return (lds_char*)sS3;
   };
-  auto vtile = [&](auto b) -> lds_char* {
-    constexpr int S = decltype(b)::value;
-    if constexpr (S == 0) return (lds_char*)sV0;
-    else if constexpr (S == 1) return (lds_char*)sV1;
-    else if constexpr (S == 2) return (lds_char*)sV2;
-    else return (lds_char*)sV3;
-  };
-  auto ptile = [&](auto b) -> int* {
-    constexpr int S = decltype(b)::value;
-    if constexpr (S == 0) return sP0;
-    else if constexpr (S == 1) return sP1;
-    else if constexpr (S == 2) return sP2;
-    else return sP3;
-  };
+  auto ktile = [&](auto b) -> lds_char* { return stage_base(b); };
+  auto vtile = [&](auto b) -> lds_char* { return stage_base(b) + C::TILE; };
+  auto ptile = [&](auto b) -> int* { return (int*)(stage_base(b) + 2 * C::TILE); };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
@@ -108,7 +105,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -205,8 +202,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     const int j0 = (tb + t) * C::BN;
     const size_t o = (size_t)j0 * kv_row_stride;
     const int rows = uniform(live ? min(C::BN, p.sk - j0) : 0);
-    ld.load_clamped(ktile(stage), kbase + o, kv_row_stride, rows);
-    ld.load_clamped(vtile(stage), vbase + o, kv_row_stride, rows);
+    ld.load_rows(ktile(stage), kbase + o, rows);
+    ld.load_rows(vtile(stage), vbase + o, rows);
     pos_load_direct((lds_char*)(ptile(stage) + wave * C::BN), pos_src, j0, rows);
   };
 
@@ -376,14 +373,190 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     }
   };
 
-  if (nt > 0) issue_tile(0, S0{}, true);
-  issue_tile(1, S1{}, nt > 1);
-  issue_tile(2, S2{}, nt > 2);
-  for (int t = 0; t < nt; t += 4) {
-    step(S0{}, t);
-    if (t + 1 < nt) step(S1{}, t + 1);
-    if (t + 2 < nt) step(S2{}, t + 2);
-    if (t + 3 < nt) step(S3{}, t + 3);
+  if constexpr (PACKED) {
+    if (nt > 0) issue_tile(0, S0{}, true);
+    issue_tile(1, S1{}, nt > 1);
+    issue_tile(2, S2{}, nt > 2);
+    for (int t = 0; t < nt; t += 4) {
+      step(S0{}, t);
+      if (t + 1 < nt) step(S1{}, t + 1);
+      if (t + 2 < nt) step(S2{}, t + 2);
+      if (t + 3 < nt) step(S3{}, t + 3);
+    }
+  } else if (nt > 0) {
+    // ---- two wave groups half a tile apart ----
+    // Waves w and w + 4 share a SIMD.  Group 1 (waves 4-7) runs the same
+    // program one barrier behind group 0, so while one group's waves run
+    // their contractions (P V of tile t, then the scores of tile t + 1) the
+    // other group's waves on the same SIMDs run the softmax of their tile.
+    static_assert(C::QB == 1, "one 32-row block per wave");
+    const int grp = uniform(wave >> 2);
+    f32x16 s[C::NKB];
+    uint32_t pk[C::NKB][8];
+    // P V of the tile in stage SP, then the scores of tile ts (stage SS) with
+    // the loads of tile ts + 2 among them (its stage, (SS + 2) % 4, held tile
+    // ts - 2, whose P V both groups have finished).  Each operand is read two
+    // MFMAs ahead of its use; the first two V^T operands (vpre) were read
+    // before the barrier that starts the phase.
+    auto pv_then_s = [&](auto sp, auto ss, int ts, const bf16x8 (&vpre)[2])
+        __attribute__((always_inline)) {
+      constexpr int SS = decltype(ss)::value;
+      using Ahead2 = std::integral_constant<int, (SS + 2) % C::NS>;
+      const lds_char* vt = vtile(sp);
+      const lds_char* kt = ktile(ss);
+      constexpr int NPV = C::BN / 16 * C::MB, NSC = C::KS * C::NKB;
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int ks2 = i / C::MB, mb = i % C::MB;
+        const int kb = ks2 >> 1, half = ks2 & 1;
+        const int rb = ks2 * 16 * D * 2;
+        const bf16x8 a = i < 2 ? vpre[i] : lds_read_tr(vt, rb + voff[0][mb], rb + voff[1][mb]);
+        const u32x4 bw = {pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2],
+                          pk[kb][4 * half + 3]};
+        oacc[0][mb] = mfma32x32x16(a, __builtin_bit_cast(bf16x8, bw), oacc[0][mb]);
+      }
+      issue_tile(ts + 2, Ahead2{}, ts + 2 < nt);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          const bf16x8 a = lds_read_b128(kt, kb * 32 * D * 2 + koff[ks]);
+          s[kb] = mfma32x32x16(a, qf[0][ks], ks == 0 ? f32x16{} : s[kb]);
+        }
+      // after MFMA i, the reads of MFMA i + 2 (two transposing reads for P V,
+      // one b128 read for the scores); the loads among the scores
+#pragma unroll
+      for (int i = 0; i < NPV + NSC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        const int j = i + 2;
+        if (j < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (j < NPV + NSC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i >= NPV && ((i - NPV) & 1) && (i - NPV) < 2 * C::VMEM)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    };
+    // the first tile's scores (and the loads of tile 2)
+    auto s_only = [&](auto ss, int ts) __attribute__((always_inline)) {
+      constexpr int SS = decltype(ss)::value;
+      using Ahead2 = std::integral_constant<int, (SS + 2) % C::NS>;
+      const lds_char* kt = ktile(ss);
+      issue_tile(ts + 2, Ahead2{}, ts + 2 < nt);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          const bf16x8 a = lds_read_b128(kt, kb * 32 * D * 2 + koff[ks]);
+          s[kb] = mfma32x32x16(a, qf[0][ks], ks == 0 ? f32x16{} : s[kb]);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < C::KS * C::NKB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + 2 < C::KS * C::NKB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if ((i & 1) && i < 2 * C::VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    };
+    // softmax of tile t (stage ST): masks, running max, exponentials -> pk,
+    // row sums; the scores stay in registers for the max-and-rescale path
+    auto softmax = [&](auto st, int t) __attribute__((always_inline)) {
+      const int* kp = ptile(st) + wave * C::BN;
+      const int kfirst = uniform(kp[0]);
+      const int klast = uniform(kp[C::BN - 1]);
+      const int valid = min(C::BN, p.sk - (tb + t) * C::BN);
+      const bool tail = valid < C::BN;
+      const bool blind = !wave_live || (causal && kfirst > wqmax);
+      const bool straddle = blind || tail || (causal && klast > bmin[0]);
+      auto exps = [&](float neg_m, float& ps0, float& ps1) __attribute__((always_inline)) {
+        ps0 = 0.f;
+        ps1 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const float e0 = fast_exp2(fmaf(s[kb][i], c, neg_m));
+            const float e1 = fast_exp2(fmaf(s[kb][i + 1], c, neg_m));
+            pk[kb][i >> 1] = pack_bf16x2(e0, e1);
+            if (i & 2) ps1 += e0 + e1; else ps0 += e0 + e1;
+          }
+      };
+      bool slow = straddle || __ballot(m_run[0] == -INFINITY) != 0;
+      float ps0 = 0.f, ps1 = 0.f;
+      if (!slow) {
+        exps(-m_run[0], ps0, ps1);
+        slow = __ballot(!(ps0 + ps1 <= 65536.0f)) != 0;
+      }
+      if (slow) {
+        asm volatile("" ::: "memory");
+        if (straddle) {
+          const uint32_t lo = (uint32_t)qs[0];
+          const uint32_t span = (uint32_t)(causal ? qpos[0] : INT_MAX) - lo;
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+              const bool hide = ((uint32_t)kp[key] - lo > span) | (key >= valid) | blind;
+              s[kb][i] = hide ? -INFINITY : s[kb][i];
+            }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
+        mt = max_halves(mt) * c;
+        if (__ballot(mt > m_run[0] + 8.0f)) {
+          asm volatile("" ::: "memory");
+          const float m_new = fmaxf(m_run[0], mt);
+          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[0] - m_new);
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) oacc[0][mb] *= alpha;
+          l_run[0] *= alpha;
+          m_run[0] = m_new;
+        }
+        exps((m_run[0] == -INFINITY) ? 0.f : -m_run[0], ps0, ps1);
+      }
+      l_run[0] += ps0 + ps1;
+    };
+    // One tile: [wait, barrier] softmax(t) [wait, barrier] P V(t) + S(t+1).
+    // Tile t + 1 must be in LDS before group 0 starts its scores; every wave
+    // waits for its share of it at both barriers (the loads of one later tile
+    // stay in flight).  The wave running its contractions raises its priority
+    // so that the softmax of the other wave on its SIMD (an older wave in
+    // group 0) does not hold back its MFMA issue.
+    auto tile = [&](auto st, auto sn, int t) __attribute__((always_inline)) {
+      wait_vmcnt<C::VMEM>();
+      barrier_only();
+      softmax(st, t);
+      bf16x8 vpre[2];
+      {
+        const lds_char* vt = vtile(st);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) vpre[i] = lds_read_tr(vt, voff[0][i], voff[1][i]);
+      }
+      wait_vmcnt<C::VMEM>();
+      barrier_only();
+      // the last tile also runs the (unused) scores of tile nt: one code path
+      __builtin_amdgcn_s_setprio(1);
+      pv_then_s(st, sn, t + 1, vpre);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    issue_tile(0, S0{}, true);
+    issue_tile(1, S1{}, nt > 1);
+    wait_vmcnt<C::VMEM>();
+    barrier_only();
+    if (grp == 1) barrier_only();  // group 1 runs one barrier behind
+    __builtin_amdgcn_s_setprio(1);
+    s_only(S0{}, 0);
+    __builtin_amdgcn_s_setprio(0);
+    for (int t = 0; t < nt; t += 4) {
+      tile(S0{}, S1{}, t);
+      if (t + 1 < nt) tile(S1{}, S2{}, t + 1);
+      if (t + 2 < nt) tile(S2{}, S3{}, t + 2);
+      if (t + 3 < nt) tile(S3{}, S0{}, t + 3);
+    }
+    if (grp == 0) barrier_only();  // same barrier count in both groups
+    wait_vmem_le<0>();
   }
 
   // ---- epilogue: normalise, then write or merge ----

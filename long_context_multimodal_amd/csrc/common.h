@@ -186,6 +186,13 @@ struct TileLoader {
 #pragma unroll
     for (int c = 0; c < ROUNDS; ++c) buffer_to_lds<16>(rs, off[c], tile + (c * THREADS + wave_base) * 16);
   }
+  // the first `rows` rows of the tile; the rows after them lie outside the
+  // buffer's range and arrive as zeros
+  __device__ __forceinline__ void load_rows(lds_char* tile, const uint16_t* base, int rows) const {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, clamp_bytes((size_t)rows * row_bytes));
+#pragma unroll
+    for (int c = 0; c < ROUNDS; ++c) buffer_to_lds<16>(rs, off[c], tile + (c * THREADS + wave_base) * 16);
+  }
   // tail tile: rows at or past `rows_left` re-read the last existing row
   __device__ __forceinline__ void load_clamped(lds_char* tile, const uint16_t* base,
                                                size_t row_stride, int rows_left) const {
@@ -215,6 +222,14 @@ template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The same wait through the builtin: the compiler's own wait insertion sees
+// it and does not wait again for the loads it retired.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // 64 key positions of a tile straight into this wave's LDS slot (lane l ->
