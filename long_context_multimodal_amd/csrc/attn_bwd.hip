@@ -61,8 +61,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char sO0[C::TILE], sO1[C::TILE];
   __shared__ __attribute__((aligned(16))) char sVrows[C::VTILE];
   // per-row statistics of the two tiles in flight, one row of 36 words per
-  // (statistic, buffer): 0 sample starts (packed), 1 LSE*log2e (+inf empty),
-  // 2 delta, 3 positions (word 32: the tile's last position)
+  // (statistic, buffer): 0 sample starts (packed), 1 -LSE/scale (-inf for
+  // empty rows and rows past sq), 2 -delta, 3 positions (word 32: the tile's
+  // last position).  Rows 1 and 2 are where the S and dP accumulators start,
+  // so that exp2(c S) is the weight and dP arrives as dP - delta.
   constexpr int SROW = 36;
   __shared__ __attribute__((aligned(16))) uint32_t sStat[4][2][SROW];
   auto sQs = [&](int b) -> const int* { return (const int*)sStat[0][b]; };
@@ -224,17 +226,19 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   };
   // Each wave converts its statistic and writes it with one store: the
   // destination row is fixed per wave, so only the lane offset is a register.
+  const float inv_scale = 1.0f / p.scale;
   auto publish_tile = [&](int buf) {
     if (lane <= C::BQ && (wave == 3 || lane < C::BQ)) {
       uint32_t val;
       if (wave == 0) {
         val = (packed && row_live) ? stat : (uint32_t)INT_MIN;
       } else if (wave == 1) {
-        // empty rows (LSE = -inf) and rows past sq get P = exp2(s c - inf) = 0
+        // -LSE / scale, the start of the S accumulator, so that c S' = c S -
+        // LSE log2(e); empty rows and rows past sq get -inf (weights 0)
         const float l = __uint_as_float(stat);
-        val = __float_as_uint((row_live && l != -INFINITY) ? l * kLog2e : INFINITY);
+        val = __float_as_uint((row_live && l != -INFINITY) ? -l * inv_scale : -INFINITY);
       } else if (wave == 2) {
-        val = row_live ? stat : 0u;
+        val = row_live ? (stat ^ 0x80000000u) : 0u;  // -delta, the start of dP
       } else {
         const int pos = p.causal ? (int)stat : kPosInf - 1;
         val = (uint32_t)((row_live || lane == C::BQ) ? pos : INT_MIN);
@@ -271,10 +275,21 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     if constexpr (packed) issue_next(Next{}, more);
     if (!packed || sees) {
       if constexpr (!packed) issue_next(Next{}, more);
-      // S = Q K^T and dP = dO V^T  (row = query, col = key)
-      f32x16 s = mfma32x32x16(lds_read_b128(qt, qoff[0]), kf[0], f32x16{});
-      f32x16 dp = mfma32x32x16(lds_read_b128(dt, qoff[0]), lds_read_b128(vrows, qoff[0]),
-                               f32x16{});
+      // S = Q K^T and dP = dO V^T  (row = query, col = key), accumulated onto
+      // -LSE/scale and -delta of their rows
+      f32x16 s0, d0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *(const f32x4*)&sL(BUF)[8 * g + 4 * hh];
+        const f32x4 d4 = *(const f32x4*)&sDl(BUF)[8 * g + 4 * hh];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s0[4 * g + e] = l4[e];
+          d0[4 * g + e] = d4[e];
+        }
+      }
+      f32x16 s = mfma32x32x16(lds_read_b128(qt, qoff[0]), kf[0], s0);
+      f32x16 dp = mfma32x32x16(lds_read_b128(dt, qoff[0]), lds_read_b128(vrows, qoff[0]), d0);
 #pragma unroll
       for (int ks = 1; ks < C::KS; ++ks) {
         s = mfma32x32x16(lds_read_b128(qt, qoff[ks]), kf[ks], s);
@@ -302,15 +317,12 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
       uint32_t pk[8], dsk[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int q = 8 * g + 4 * hh;  // rows q .. q+3 of this lane
-        const f32x4 lq = *(const f32x4*)&sL(BUF)[q];
-        const f32x4 dq = *(const f32x4*)&sDl(BUF)[q];
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pe = fast_exp2(fmaf(s[4 * g + e], c, -lq[e]));
+          const float pe = fast_exp2(s[4 * g + e] * c);
           pv[e] = pe;
-          dsv[e] = pe * (dp[4 * g + e] - dq[e]);
+          dsv[e] = pe * dp[4 * g + e];
         }
         pk[2 * g] = pack_bf16x2(pv[0], pv[1]);
         pk[2 * g + 1] = pack_bf16x2(pv[2], pv[3]);
@@ -630,8 +642,11 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
       for (int kb = 0; kb < C::NKB; ++kb) {  // 32 keys at a time
         const int rb = kb * 32 * D * 2;
         if (!packed && kb == 0) issue_tile(t + 1, Next{}, more);
+        f32x16 dinit;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dinit[i] = -delta;  // dP accumulates onto -delta
         f32x16 s = mfma32x32x16(lds_read_b128(kt, rb + koff[0]), qf[0], f32x16{});
-        f32x16 dp = mfma32x32x16(lds_read_b128(vt, rb + koff[0]), df[0], f32x16{});
+        f32x16 dp = mfma32x32x16(lds_read_b128(vt, rb + koff[0]), df[0], dinit);
 #pragma unroll
         for (int ks = 1; ks < C::KS; ++ks) {
           s = mfma32x32x16(lds_read_b128(kt, rb + koff[ks]), qf[ks], s);
@@ -662,7 +677,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
         for (int i = 0; i < 16; i += 2) {
           const float p0 = fast_exp2(fmaf(s[i], c, -lse2));
           const float p1 = fast_exp2(fmaf(s[i + 1], c, -lse2));
-          dsk[i >> 1] = pack_bf16x2(p0 * (dp[i] - delta), p1 * (dp[i + 1] - delta));
+          dsk[i >> 1] = pack_bf16x2(p0 * dp[i], p1 * dp[i + 1]);
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
