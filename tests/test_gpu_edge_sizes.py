@@ -44,6 +44,11 @@ CASES = [  # (sq, sk, hq, hkv, d, layout)
     (256, 256, 2, 1, 128, "interleaved"),   # whole tiles, no tail
     (128, 64, 3, 3, 128, "keys_after"),
     (65, 200, 8, 2, 64, "keys_before"),
+    # 2, 3 and 7 key tiles at d = 128: the forward's tile loop is unrolled
+    # four stages deep, and these leave it after its second and third stage
+    (96, 128, 2, 2, 128, "interleaved"),
+    (200, 190, 3, 1, 128, "keys_before"),
+    (300, 448, 4, 2, 128, "keys_before"),
 ]
 
 
