@@ -645,20 +645,24 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
         f32x16 dinit;
 #pragma unroll
         for (int i = 0; i < 16; ++i) dinit[i] = -delta;  // dP accumulates onto -delta
-        f32x16 s = mfma32x32x16(lds_read_b128(kt, rb + koff[0]), qf[0], f32x16{});
-        f32x16 dp = mfma32x32x16(lds_read_b128(vt, rb + koff[0]), df[0], dinit);
+        // K / V operands read two contractions ahead of their use (S and dP
+        // alternate); a scheduling barrier after every contraction holds that
+        // order, which the scheduler otherwise folds back to read, wait, MFMA
+        constexpr int LA = 2;
+        bf16x8 op[2 * C::KS];
+        auto rd = [&](int i) { return lds_read_b128((i & 1) ? vt : kt, rb + koff[i >> 1]); };
 #pragma unroll
-        for (int ks = 1; ks < C::KS; ++ks) {
-          s = mfma32x32x16(lds_read_b128(kt, rb + koff[ks]), qf[ks], s);
-          dp = mfma32x32x16(lds_read_b128(vt, rb + koff[ks]), df[ks], dp);
-        }
-        if (kb == 0) {
-          // the next tile's loads spread between the contractions
+        for (int i = 0; i < LA; ++i) op[i] = rd(i);
+        f32x16 s = f32x16{};
+        f32x16 dp = dinit;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          }
+        for (int i = 0; i < 2 * C::KS; ++i) {
+          if (i + LA < 2 * C::KS) op[i + LA] = rd(i + LA);
+          if (i & 1)
+            dp = mfma32x32x16(op[i], df[i >> 1], dp);
+          else
+            s = mfma32x32x16(op[i], qf[i >> 1], s);
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (straddle) {
           asm volatile("" ::: "memory");
