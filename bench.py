@@ -368,6 +368,9 @@ def main():
     ap.add_argument("--native-ring", action="store_true",
                     help="also time the step with the ring loop in the library (mmsp_ring_forward "
                          "/ mmsp_ring_backward) and check its outputs against the Python driver's")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="packed samples: keep the kernels' built-in tile order instead of the "
+                         "work-ordered tile plan made each step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -463,25 +466,39 @@ def main():
                                          with_inverse=False)
         return perm, first, qs
 
+    plan_bufs = [None]
+
+    def tile_plans(qp, qs, kps):
+        """Work-ordered tile plans of the step's chunks (packed samples): one
+        per chunk, shared by the forward and the backward, buffers reused."""
+        if qs is None:
+            return None
+        if args.no_plan:
+            return [None] * len(kps)
+        plan_bufs[0] = ring.packed_plans(qp, qs, kps, plans=plan_bufs[0])
+        return plan_bufs[0]
+
     def step(received=args.ring_copy):
         perm, first, qs = balance()
         qp = perm[rank * w.shard:(rank + 1) * w.shard]
         kps = [perm[c * w.chunk:(c + 1) * w.chunk] for c in range(w.n_chunks)]
+        plans = tile_plans(qp, qs, kps)
         qq, kk = rope_in(qp, kps) if theta else (q, ks)
         if received:
             ring.ring_forward_received(qq, kk, vs, qp, kps, rx, rank=rank, fused=not args.unfused,
-                                       o=o, lse=lse, o_final=o16, timer=timer, q_start=qs)
+                                       o=o, lse=lse, o_final=o16, timer=timer, q_start=qs,
+                                       plans=plans)
             if w.backward:
                 ring.ring_backward_received(qq, kk, vs, dout, o16, lse, qp, kps, rx, rank=rank,
                                             dq=dq, dks=dks, dvs=dvs, dk_sent=dk_sent,
                                             dv_sent=dv_sent, delta=delta, timer=timer,
-                                            q_start=qs)
+                                            q_start=qs, plans=plans)
         else:
             ring.ring_forward(qq, kk, vs, qp, kps, rank=rank, fused=not args.unfused, o=o,
-                              lse=lse, o_final=o16, timer=timer, q_start=qs)
+                              lse=lse, o_final=o16, timer=timer, q_start=qs, plans=plans)
             if w.backward:
                 ring.ring_backward(qq, kk, vs, dout, o16, lse, qp, kps, rank=rank, dq=dq, dks=dks,
-                                   dvs=dvs, delta=delta, timer=timer, q_start=qs)
+                                   dvs=dvs, delta=delta, timer=timer, q_start=qs, plans=plans)
         if theta and w.backward:
             rope_out(qp, kps)
         return perm, first
@@ -595,6 +612,8 @@ def main():
             "layout": w.layout, "rank": rank,
             "pass": "fwd+bwd" if w.backward else "fwd",
             "merge": "separate" if args.unfused else "fused into chunk epilogue",
+            "tile_order": ("built-in" if w.layout != "packed" or args.no_plan
+                           else "work-ordered plan per chunk"),
             "chunks": ("received by double-buffered copies" if args.ring_copy
                        else "resident in HBM"),
             "rope_theta": theta,

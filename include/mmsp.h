@@ -229,12 +229,47 @@ int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32
  * q_start int32 [sq] (device, required): first position of query i's sample,
  *         q_start[i] <= q_pos[i], non-decreasing in i (as mmsp_shard_balance_
  *         packed produces it).  flags must include MMSP_CAUSAL.
+ * plan    (nullable) tile plan from mmsp_attn_packed_plan for these
+ *         positions, plan_bytes its size (below); NULL: built-in tile order.
  */
 int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
                                const int32_t* q_pos, const int32_t* q_start,
-                               const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
-                               int32_t hkv, int32_t d, float scale, uint32_t flags, float* o,
-                               float* lse, hipStream_t stream);
+                               const int32_t* k_pos, const void* plan, size_t plan_bytes,
+                               int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d,
+                               float scale, uint32_t flags, float* o, float* lse,
+                               hipStream_t stream);
+
+/* ---- tile plan of the packed attention calls --------------------------------
+ * Scheduling only, not part of the method: the results of the packed calls
+ * are the same bit for bit with or without a plan.  With packed samples
+ * ("LongVILA Guide ...", "Critical Operational Best Practices") the work of
+ * a workgroup depends on the samples its tile holds, and the built-in tile
+ * order (made for the plain causal shard) can leave the heaviest tiles to the
+ * end of the launch.  mmsp_attn_packed_plan counts each tile's work from the
+ * positions and lists the tiles heaviest first for the forward, the dQ and
+ * the dK/dV kernels; passed as `plan` to mmsp_attn_fwd_chunk_packed and
+ * mmsp_attn_bwd_chunk_packed, the kernels take their tiles in that order.
+ * One plan serves the forward and the backward of the same (q_pos, q_start,
+ * k_pos).
+ *
+ * plan        device buffer of plan_bytes >= mmsp_attn_packed_plan_bytes(sq,
+ *             sk) bytes (32 + 8 * (ceil(sq/256) + ceil(sq/128) + ceil(sk/128))),
+ *             owned by the caller; written by mmsp_attn_packed_plan on
+ *             `stream`.  NULL in the attention calls keeps the built-in order.
+ * q_pos, q_start, k_pos as in mmsp_attn_fwd_chunk_packed; sq, sk >= 1.
+ * A plan carries the sq and sk it was made for; an attention call whose sizes
+ * differ ignores it (built-in order).  A plan made from other positions of
+ * the same sizes is still a valid order (same results, other speed).
+ * Errors: NULL pointer (MMSP_ERR_NULL), sq or sk < 1 (MMSP_ERR_SHAPE),
+ * plan_bytes too small (MMSP_ERR_WORKSPACE; also from the attention calls
+ * given a non-NULL plan).  mmsp_attn_packed_plan_bytes returns 0 for sizes
+ * below 1.  Cost: two small launches; tile lists longer than 32768 entries
+ * are left in index order.
+ */
+size_t mmsp_attn_packed_plan_bytes(int32_t sq, int32_t sk);
+int mmsp_attn_packed_plan(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
+                          int32_t sq, int32_t sk, void* plan, size_t plan_bytes,
+                          hipStream_t stream);
 
 /* ---- a3: log-sum-exp merge of two chunk results ---------------------------
  * The page's ring loop ("Implementation ...") adds each step's output into an
@@ -291,14 +326,15 @@ int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void*
 /* ---- a6 with packed samples -------------------------------------------------
  * As mmsp_attn_bwd_chunk with the packed-sample visibility of
  * mmsp_attn_fwd_chunk_packed (q_start as there; flags must include
- * MMSP_CAUSAL); lse is the final LSE of the packed forward.
+ * MMSP_CAUSAL); lse is the final LSE of the packed forward.  plan and
+ * plan_bytes as in mmsp_attn_fwd_chunk_packed.
  */
 int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, const void* dout,
                                const float* lse, const float* delta, const int32_t* q_pos,
-                               const int32_t* q_start, const int32_t* k_pos, int32_t sq,
-                               int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
-                               uint32_t flags, float* dq_acc, float* dk, float* dv,
-                               hipStream_t stream);
+                               const int32_t* q_start, const int32_t* k_pos, const void* plan,
+                               size_t plan_bytes, int32_t sq, int32_t sk, int32_t hq,
+                               int32_t hkv, int32_t d, float scale, uint32_t flags,
+                               float* dq_acc, float* dk, float* dv, hipStream_t stream);
 
 /* ---- a4: one rank's ring loop over resident chunks -----------------------
  * "LongVILA Guide ...", section "Implementation: PyTorch Distributed
@@ -314,7 +350,8 @@ int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, cons
  * n_chunks DEVICE pointers, read during the call only.  Every chunk has sk
  * keys.  q, q_pos, q_start, scale and the shapes are as in
  * mmsp_attn_fwd_chunk(_packed); q_start (nullable) selects packed samples
- * and needs MMSP_CAUSAL.  0 <= rank < n_chunks.
+ * and needs MMSP_CAUSAL (these loops use the built-in tile order: no tile
+ * plan).  0 <= rank < n_chunks.
  *
  * mmsp_ring_forward: the first step writes (o fp32 [sq][hq][d], lse fp32
  *   [hq][sq]), later steps merge into them (MMSP_ACCUMULATE); then, if

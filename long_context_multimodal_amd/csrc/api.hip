@@ -38,7 +38,7 @@ namespace {
 int attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_pos,
              const int32_t* q_start, const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
              int32_t hkv, int32_t d, float scale, uint32_t flags, float* o, float* lse,
-             hipStream_t stream) {
+             const int32_t* plan, hipStream_t stream) {
   if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE)) != 0) return MMSP_ERR_UNSUPPORTED;
   const bool causal = (flags & MMSP_CAUSAL) != 0;
   if (!q || !k || !v || !o || !lse) return MMSP_ERR_NULL;
@@ -64,13 +64,16 @@ int attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_pos,
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal ? 1 : 0;
   p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
+  p.plan = plan;
+  p.plan_off = mmsp::plan_shape(sq, sk).fwd_off();
   return check_hip(mmsp::launch_attn_fwd(p, d, as_stream(stream)));
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse,
              const float* delta, const int32_t* q_pos, const int32_t* q_start,
              const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d,
-             float scale, uint32_t flags, float* dq_acc, float* dk, float* dv, hipStream_t stream) {
+             float scale, uint32_t flags, float* dq_acc, float* dk, float* dv, const int32_t* plan,
+             hipStream_t stream) {
   if ((flags & ~(uint32_t)(MMSP_CAUSAL | MMSP_ACCUMULATE | MMSP_BWD_NO_DQ | MMSP_BWD_NO_DKDV)) !=
       0)
     return MMSP_ERR_UNSUPPORTED;
@@ -111,7 +114,18 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* dout, cons
   p.accumulate = (flags & MMSP_ACCUMULATE) ? 1 : 0;
   p.run_dkdv = run_dkdv ? 1 : 0;
   p.run_dq = run_dq ? 1 : 0;
+  const mmsp::PlanShape ps = mmsp::plan_shape(sq, sk);
+  p.plan = plan;
+  p.plan_dq_off = ps.dq_off();
+  p.plan_dkdv_off = ps.dkdv_off();
   return check_hip(mmsp::launch_attn_bwd(p, d, as_stream(stream)));
+}
+
+// A tile plan given to a packed call must be as large as its sizes need.
+int check_plan(const void* plan, size_t plan_bytes, int32_t sq, int32_t sk) {
+  if (plan == nullptr) return MMSP_OK;
+  if (sq <= 0 || sk <= 0) return MMSP_ERR_SHAPE;
+  return plan_bytes < mmsp::plan_shape(sq, sk).bytes() ? MMSP_ERR_WORKSPACE : MMSP_OK;
 }
 
 }  // namespace
@@ -255,18 +269,36 @@ int mmsp_attn_fwd_chunk(const void* q, const void* k, const void* v, const int32
                         int32_t d, float scale, uint32_t flags, float* o, float* lse,
                         hipStream_t stream) {
   return attn_fwd(q, k, v, q_pos, nullptr, k_pos, sq, sk, hq, hkv, d, scale, flags, o, lse,
-                  stream);
+                  nullptr, stream);
 }
 
 int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
                                const int32_t* q_pos, const int32_t* q_start,
-                               const int32_t* k_pos, int32_t sq, int32_t sk, int32_t hq,
-                               int32_t hkv, int32_t d, float scale, uint32_t flags, float* o,
-                               float* lse, hipStream_t stream) {
+                               const int32_t* k_pos, const void* plan, size_t plan_bytes,
+                               int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d,
+                               float scale, uint32_t flags, float* o, float* lse,
+                               hipStream_t stream) {
   if (!(flags & MMSP_CAUSAL)) return MMSP_ERR_UNSUPPORTED;
   if (!q_start) return MMSP_ERR_NULL;
+  const int st = check_plan(plan, plan_bytes, sq, sk);
+  if (st != MMSP_OK) return st;
   return attn_fwd(q, k, v, q_pos, q_start, k_pos, sq, sk, hq, hkv, d, scale, flags, o, lse,
-                  stream);
+                  static_cast<const int32_t*>(plan), stream);
+}
+
+size_t mmsp_attn_packed_plan_bytes(int32_t sq, int32_t sk) {
+  if (sq <= 0 || sk <= 0) return 0;
+  return mmsp::plan_shape(sq, sk).bytes();
+}
+
+int mmsp_attn_packed_plan(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
+                          int32_t sq, int32_t sk, void* plan, size_t plan_bytes,
+                          hipStream_t stream) {
+  if (!q_pos || !q_start || !k_pos || !plan) return MMSP_ERR_NULL;
+  if (sq <= 0 || sk <= 0) return MMSP_ERR_SHAPE;
+  if (plan_bytes < mmsp::plan_shape(sq, sk).bytes()) return MMSP_ERR_WORKSPACE;
+  return check_hip(mmsp::launch_tile_plan(q_pos, q_start, k_pos, sq, sk,
+                                          static_cast<int32_t*>(plan), as_stream(stream)));
 }
 
 int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
@@ -299,19 +331,21 @@ int mmsp_attn_bwd_chunk(const void* q, const void* k, const void* v, const void*
                         int32_t d, float scale, uint32_t flags, float* dq_acc, float* dk,
                         float* dv, hipStream_t stream) {
   return attn_bwd(q, k, v, dout, lse, delta, q_pos, nullptr, k_pos, sq, sk, hq, hkv, d, scale,
-                  flags, dq_acc, dk, dv, stream);
+                  flags, dq_acc, dk, dv, nullptr, stream);
 }
 
 int mmsp_attn_bwd_chunk_packed(const void* q, const void* k, const void* v, const void* dout,
                                const float* lse, const float* delta, const int32_t* q_pos,
-                               const int32_t* q_start, const int32_t* k_pos, int32_t sq,
-                               int32_t sk, int32_t hq, int32_t hkv, int32_t d, float scale,
-                               uint32_t flags, float* dq_acc, float* dk, float* dv,
-                               hipStream_t stream) {
+                               const int32_t* q_start, const int32_t* k_pos, const void* plan,
+                               size_t plan_bytes, int32_t sq, int32_t sk, int32_t hq,
+                               int32_t hkv, int32_t d, float scale, uint32_t flags,
+                               float* dq_acc, float* dk, float* dv, hipStream_t stream) {
   if (!(flags & MMSP_CAUSAL)) return MMSP_ERR_UNSUPPORTED;
   if (!q_start) return MMSP_ERR_NULL;
+  const int st = check_plan(plan, plan_bytes, sq, sk);
+  if (st != MMSP_OK) return st;
   return attn_bwd(q, k, v, dout, lse, delta, q_pos, q_start, k_pos, sq, sk, hq, hkv, d, scale,
-                  flags, dq_acc, dk, dv, stream);
+                  flags, dq_acc, dk, dv, static_cast<const int32_t*>(plan), stream);
 }
 
 // One rank's ring loop: chunk (rank - t) mod n_chunks at step t.  Every
@@ -335,7 +369,7 @@ int mmsp_ring_forward(const void* q, const void* const* k_chunks, const void* co
     const int c = ((rank - t) % n_chunks + n_chunks) % n_chunks;
     const uint32_t f = flags | (t > 0 ? (uint32_t)MMSP_ACCUMULATE : 0u);
     st = attn_fwd(q, k_chunks[c], v_chunks[c], q_pos, q_start, causal ? k_pos_chunks[c] : nullptr,
-                  sq, sk, hq, hkv, d, scale, f, o, lse, stream);
+                  sq, sk, hq, hkv, d, scale, f, o, lse, nullptr, stream);
     if (st != MMSP_OK) return st;
   }
   if (o_final_bf16 == nullptr) return MMSP_OK;
@@ -373,7 +407,7 @@ int mmsp_ring_backward(const void* q, const void* const* k_chunks, const void* c
     const int c = ((rank - t) % n_chunks + n_chunks) % n_chunks;
     st = attn_bwd(q, k_chunks[c], v_chunks[c], dout, lse, delta, q_pos, q_start,
                   causal ? k_pos_chunks[c] : nullptr, sq, sk, hq, hkv, d, scale, flags, dq,
-                  dk_chunks[c], dv_chunks[c], stream);
+                  dk_chunks[c], dv_chunks[c], nullptr, stream);
     if (st != MMSP_OK) return st;
   }
   return MMSP_OK;

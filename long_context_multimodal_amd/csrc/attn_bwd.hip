@@ -87,9 +87,12 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   const int hh = lane >> 5;
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int kvh = logical / p.n_ktiles;
+  int kvh = logical / p.n_ktiles;
   // early keys see more queries: their end of the range is dispatched first
-  const int kt = p.n_ktiles - 1 - heavy_first_tile(logical % p.n_ktiles, p.n_ktiles, gridDim.x);
+  int kt = p.n_ktiles - 1 - heavy_first_tile(logical % p.n_ktiles, p.n_ktiles, gridDim.x);
+  // packed samples: tiles heaviest first from the plan, when one is given
+  if (PACKED && plan_fits(p.plan, kPlanMagic, p.sq, p.sk))
+    planned_tile(blockIdx.x, p.n_ktiles, p.hkv, p.plan + p.plan_dkdv_off, kvh, kt);
   const int j0 = kt * C::BK;
   const int key = j0 + wave * 32 + l32;
   const bool key_ok = key < p.sk;
@@ -499,8 +502,11 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   const int hh = lane >> 5;
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int h = logical / p.n_qtiles;
-  const int qt = heavy_first_tile(logical % p.n_qtiles, p.n_qtiles, gridDim.x);
+  int h = logical / p.n_qtiles;
+  int qt = heavy_first_tile(logical % p.n_qtiles, p.n_qtiles, gridDim.x);
+  // packed samples: tiles heaviest first from the plan, when one is given
+  if (PACKED && plan_fits(p.plan, kPlanMagic, p.sq, p.sk))
+    planned_tile(blockIdx.x, p.n_qtiles, p.hq, p.plan + p.plan_dq_off, h, qt);
   const int kvh = h / p.group;
   const int q0 = qt * C::BM;
   const int row = q0 + wave * 32 + l32;
@@ -757,8 +763,13 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
+static_assert(DkdvCfg<64>::BK == DkdvCfg<128>::BK && DkdvCfg<64>::BQ == DkdvCfg<128>::BQ &&
+                  DqCfg<64>::BM == DqCfg<128>::BM && DqCfg<64>::BN == DqCfg<128>::BN,
+              "tile plans are laid out for one tile shape per kernel");
 int bwd_keys_per_block() { return DkdvCfg<128>::BK; }
 int bwd_rows_per_block() { return DqCfg<128>::BM; }
+int dkdv_rows_per_tile() { return DkdvCfg<128>::BQ; }
+int dq_keys_per_tile() { return DqCfg<128>::BN; }
 
 hipError_t launch_attn_bwd(const BwdParams& p, int d, hipStream_t stream) {
   return d == 64 ? launch_bwd_d<64>(p, stream) : launch_bwd_d<128>(p, stream);

@@ -110,8 +110,11 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   const int hh = lane >> 5;
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int h = logical / p.n_qtiles;
-  const int qt = heavy_first_tile(logical % p.n_qtiles, p.n_qtiles, gridDim.x);
+  int h = logical / p.n_qtiles;
+  int qt = heavy_first_tile(logical % p.n_qtiles, p.n_qtiles, gridDim.x);
+  // packed samples: tiles heaviest first from the plan, when one is given
+  if (PACKED && plan_fits(p.plan, kPlanMagic, p.sq, p.sk))
+    planned_tile(blockIdx.x, p.n_qtiles, p.hq, p.plan + p.plan_off, h, qt);
   const int kvh = h / p.group;
   const int q0 = qt * C::BM;
   const int wr0 = q0 + wave * 32 * C::QB;  // first row of this wave
@@ -624,7 +627,10 @@ hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
+static_assert(FwdCfg<64>::BM == FwdCfg<128>::BM && FwdCfg<64>::BN == FwdCfg<128>::BN,
+              "tile plans are laid out for one tile shape per kernel");
 int fwd_rows_per_block() { return FwdCfg<128>::BM; }
+int fwd_keys_per_tile() { return FwdCfg<128>::BN; }
 
 hipError_t launch_attn_fwd(const FwdParams& p, int d, hipStream_t stream) {
   return d == 64 ? launch_fwd_d<64>(p, stream) : launch_fwd_d<128>(p, stream);

@@ -112,6 +112,33 @@ __device__ __forceinline__ int heavy_first_tile(int i, int n, int grid) {
   return (blk << 3) | (i & 7);
 }
 
+// Head and tile of workgroup b from a work-ordered tile list (heaviest first)
+// of n tiles per head, H heads.  As with xcd_logical_block, each XCD keeps a
+// contiguous share of the heads (with H a multiple of 8); within it the heads
+// take turns, so every XCD starts with the heaviest tiles of all its heads
+// and ends with the lightest.  Otherwise heads simply take turns.  A list
+// entry outside [0, n) is clamped (a damaged list can give wrong results,
+// never an access out of bounds).
+__device__ __forceinline__ void planned_tile(int b, int n, int H, const int32_t* list, int& h,
+                                             int& t) {
+  int j;
+  if ((H & 7) == 0) {
+    const int hx = H >> 3;
+    j = (b >> 3) / hx;
+    h = (b & 7) * hx + (b >> 3) % hx;
+  } else {
+    j = b / H;
+    h = b % H;
+  }
+  t = min(max(uniform(list[j]), 0), n - 1);
+}
+
+// Whether a tile plan (layout in kernels.h) was made for these sizes.
+__device__ __forceinline__ bool plan_fits(const int32_t* plan, int32_t magic, int sq, int sk) {
+  if (plan == nullptr) return false;
+  return uniform(plan[0]) == magic && uniform(plan[1]) == sq && uniform(plan[2]) == sk;
+}
+
 // ---- swizzled LDS tiles -----------------------------------------------------
 template <int D>
 __device__ __forceinline__ constexpr int swz(int r) {

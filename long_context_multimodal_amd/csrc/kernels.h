@@ -19,6 +19,10 @@ struct FwdParams {
   int sq, sk, hq, hkv, group, n_qtiles;
   float scale_log2;  // scale * log2(e)
   int causal, accumulate;
+  // packed samples: a tile plan (tile_plan.hip) or null; plan_off is the
+  // offset of the forward's tile list in it
+  const int32_t* plan;
+  int plan_off;
 };
 
 struct BwdParams {
@@ -39,9 +43,34 @@ struct BwdParams {
   float scale_log2;
   int causal, accumulate;
   int run_dkdv, run_dq;  // which of the two kernels to enqueue
+  // packed samples: a tile plan (tile_plan.hip) or null, with the offsets of
+  // the dQ kernel's and the dK/dV kernel's tile lists in it
+  const int32_t* plan;
+  int plan_dq_off, plan_dkdv_off;
 };
 
+// Tile plan of the packed attention kernels: int32 words, a header
+// {kPlanMagic, sq, sk, n_fwd, n_dq, n_dkdv, 0, 0}, then three tile lists,
+// heaviest tile first (the forward's query tiles, the dQ kernel's query tiles,
+// the dK/dV kernel's key tiles), then the work of each tile in the same three
+// sections, by tile index.  A kernel uses a plan only when the header names
+// its own sq and sk; otherwise it keeps its built-in order.
+constexpr int32_t kPlanMagic = 0x4e414c50;
+constexpr int kPlanHeader = 8;
+struct PlanShape {
+  int n_fwd, n_dq, n_dkdv;
+  int fwd_off() const { return kPlanHeader; }
+  int dq_off() const { return kPlanHeader + n_fwd; }
+  int dkdv_off() const { return kPlanHeader + n_fwd + n_dq; }
+  int work_off() const { return kPlanHeader + n_fwd + n_dq + n_dkdv; }
+  size_t bytes() const { return 4 * (size_t)(kPlanHeader + 2 * (n_fwd + n_dq + n_dkdv)); }
+};
+PlanShape plan_shape(int sq, int sk);
+hipError_t launch_tile_plan(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
+                            int sq, int sk, int32_t* plan, hipStream_t stream);
+
 int fwd_rows_per_block();
+int fwd_keys_per_tile();
 hipError_t launch_attn_fwd(const FwdParams& p, int d, hipStream_t stream);
 
 hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part,
@@ -53,6 +82,8 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dout, int sq
 
 int bwd_keys_per_block();
 int bwd_rows_per_block();
+int dkdv_rows_per_tile();
+int dq_keys_per_tile();
 hipError_t launch_attn_bwd(const BwdParams& p, int d, hipStream_t stream);
 
 // shard balance: vis/owner scratch of n/g int32 each (MODALITY only)

@@ -1,0 +1,163 @@
+// Work-ordered tile lists for the packed attention kernels.
+//
+// With packed samples ("LongVILA Guide: 2M Context Multi-Modal AI Model",
+// section "Critical Operational Best Practices": several videos share one
+// buffer, with reset attention masks) the work of a workgroup varies with the
+// samples its tile holds: a query tile whose rows start a sample sees few
+// keys, one at the end of a long sample sees many, and a key tile past every
+// sample start of the shard sees none.  The kernels' built-in order assumes
+// the plain causal shape (work growing with the tile index), which for packed
+// shards leaves the heaviest tiles to the last round of workgroups.  These
+// kernels count each tile's work from the positions, with the same ranges the
+// attention kernels compute, and list the tiles heaviest first (longest
+// processing time first list scheduling); the attention kernels then take
+// their tiles from the lists.  Any order gives the same results bit for bit:
+// each workgroup's arithmetic does not depend on when it runs.
+#include "common.h"
+#include "kernels.h"
+
+namespace mmsp {
+namespace {
+
+struct PlanArgs {
+  const int32_t* q_pos;
+  const int32_t* q_start;
+  const int32_t* k_pos;
+  int sq, sk;
+  int fwd_bm, fwd_bn;    // forward: query rows per workgroup, keys per tile
+  int dq_bm, dq_bn;      // dQ kernel: query rows per workgroup, keys per tile
+  int dkdv_bk, dkdv_bq;  // dK/dV kernel: keys per workgroup, query rows per tile
+  int n_fwd, n_dq, n_dkdv;
+  int fwd_off, dq_off, dkdv_off, work_off;
+  int32_t* plan;
+};
+
+// Entries of the non-decreasing array a[0, n) below xa, and of b[0, n) at or
+// below xb: two branch-free binary searches stepped together, so each level
+// costs one memory round trip for both.
+__device__ __forceinline__ void count_two(const int32_t* a, int xa, const int32_t* b, int xb,
+                                          int n, int& ca, int& cb) {
+  int step = 1;
+  while (step <= n) step <<= 1;
+  int pa = 0, pb = 0;
+  for (step >>= 1; step > 0; step >>= 1) {
+    if (pa + step <= n && a[pa + step - 1] < xa) pa += step;
+    if (pb + step <= n && b[pb + step - 1] <= xb) pb += step;
+  }
+  ca = pa;
+  cb = pb;
+}
+
+// Work of every tile, in tiles of the kernel's inner loop: key tiles for the
+// query-stationary forward and dQ kernels (from the first key at or after the
+// tile's smallest sample start to the last key at or before its largest
+// position), query tiles for the key-stationary dK/dV kernel (from the first
+// query at or after the tile's smallest key position to the last query whose
+// sample starts at or before its largest one).
+__global__ void __launch_bounds__(256) plan_work_kernel(PlanArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.n_fwd + a.n_dq + a.n_dkdv) return;
+  int w;
+  if (i < a.n_fwd + a.n_dq) {
+    const bool fwd = i < a.n_fwd;
+    const int t = fwd ? i : i - a.n_fwd;
+    const int bm = fwd ? a.fwd_bm : a.dq_bm, bn = fwd ? a.fwd_bn : a.dq_bn;
+    const int q0 = t * bm;
+    const int qmax = a.q_pos[min(q0 + bm - 1, a.sq - 1)];
+    int kbeg, nk;
+    count_two(a.k_pos, a.q_start[q0], a.k_pos, qmax, a.sk, kbeg, nk);
+    w = max(0, (nk + bn - 1) / bn - kbeg / bn);
+  } else {
+    const int t = i - a.n_fwd - a.n_dq;
+    const int j0 = t * a.dkdv_bk;
+    const int kmin = a.k_pos[j0], kmax = a.k_pos[min(j0 + a.dkdv_bk - 1, a.sk - 1)];
+    int qbeg, qend;
+    count_two(a.q_pos, kmin, a.q_start, kmax, a.sq, qbeg, qend);
+    w = max(0, (qend + a.dkdv_bq - 1) / a.dkdv_bq - qbeg / a.dkdv_bq);
+  }
+  a.plan[a.work_off + i] = w;
+}
+
+// Sections longer than this keep index order: ranking costs n^2 compares.
+constexpr int kMaxRanked = 1 << 15;
+
+// One thread per tile of section blockIdx.y: its rank among the section's
+// tiles by descending work, ties by ascending index, is its slot in the list.
+__global__ void __launch_bounds__(256) plan_order_kernel(PlanArgs a) {
+  __shared__ int sw[256];
+  const int sec = blockIdx.y;
+  const int n = sec == 0 ? a.n_fwd : sec == 1 ? a.n_dq : a.n_dkdv;
+  const int list = sec == 0 ? a.fwd_off : sec == 1 ? a.dq_off : a.dkdv_off;
+  const int work = a.work_off + (sec == 0 ? 0 : sec == 1 ? a.n_fwd : a.n_fwd + a.n_dq);
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.x * blockDim.x >= n) return;  // whole block past the section
+  if (n > kMaxRanked) {
+    if (i < n) a.plan[list + i] = i;
+  } else {
+    const int wi = i < n ? a.plan[work + i] : 0;
+    int rank = 0;
+    for (int base = 0; base < n; base += 256) {
+      const int j = base + (int)threadIdx.x;
+      sw[threadIdx.x] = j < n ? a.plan[work + j] : -1;  // -1: below every work
+      __syncthreads();
+      const int m = min(256, n - base);
+      for (int k = 0; k < m; ++k) {
+        const int wj = sw[k];
+        rank += (wj > wi) || (wj == wi && base + k < i);
+      }
+      __syncthreads();
+    }
+    if (i < n) a.plan[list + rank] = i;
+  }
+  if (sec == 0 && i == 0) {
+    a.plan[0] = kPlanMagic;
+    a.plan[1] = a.sq;
+    a.plan[2] = a.sk;
+    a.plan[3] = a.n_fwd;
+    a.plan[4] = a.n_dq;
+    a.plan[5] = a.n_dkdv;
+    a.plan[6] = 0;
+    a.plan[7] = 0;
+  }
+}
+
+}  // namespace
+
+PlanShape plan_shape(int sq, int sk) {
+  const int fb = fwd_rows_per_block(), qb = bwd_rows_per_block(), kb = bwd_keys_per_block();
+  return PlanShape{(sq + fb - 1) / fb, (sq + qb - 1) / qb, (sk + kb - 1) / kb};
+}
+
+hipError_t launch_tile_plan(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
+                            int sq, int sk, int32_t* plan, hipStream_t stream) {
+  const PlanShape s = plan_shape(sq, sk);
+  PlanArgs a;
+  a.q_pos = q_pos;
+  a.q_start = q_start;
+  a.k_pos = k_pos;
+  a.sq = sq;
+  a.sk = sk;
+  a.fwd_bm = fwd_rows_per_block();
+  a.fwd_bn = fwd_keys_per_tile();
+  a.dq_bm = bwd_rows_per_block();
+  a.dq_bn = dq_keys_per_tile();
+  a.dkdv_bk = bwd_keys_per_block();
+  a.dkdv_bq = dkdv_rows_per_tile();
+  a.n_fwd = s.n_fwd;
+  a.n_dq = s.n_dq;
+  a.n_dkdv = s.n_dkdv;
+  a.fwd_off = s.fwd_off();
+  a.dq_off = s.dq_off();
+  a.dkdv_off = s.dkdv_off();
+  a.work_off = s.work_off();
+  a.plan = plan;
+  const int total = s.n_fwd + s.n_dq + s.n_dkdv;
+  hipLaunchKernelGGL(plan_work_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nmax = max(s.n_fwd, max(s.n_dq, s.n_dkdv));
+  hipLaunchKernelGGL(plan_order_kernel, dim3((nmax + 255) / 256, 3), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mmsp

@@ -48,11 +48,14 @@ SIGNATURES = {
     "mmsp_shard_scatter": (ctypes.c_int, [_VP, _I64, _VP, _I64, _I64, _VP, _VP]),
     "mmsp_rope": (ctypes.c_int, [_VP, _VP, _I32, _VP, _I32, _I32, _I32, ctypes.c_double, _I32,
                                  _VP]),
-    "mmsp_attn_fwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
-                                                  _I32, _I32, _F32, _U32, _VP, _VP, _VP]),
+    "mmsp_attn_fwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I32,
+                                                  _I32, _I32, _I32, _I32, _F32, _U32, _VP, _VP,
+                                                  _VP]),
     "mmsp_attn_bwd_chunk_packed": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                                  _I32, _I32, _I32, _I32, _I32, _F32, _U32, _VP,
-                                                  _VP, _VP, _VP]),
+                                                  _VP, _SZ, _I32, _I32, _I32, _I32, _I32, _F32,
+                                                  _U32, _VP, _VP, _VP, _VP]),
+    "mmsp_attn_packed_plan_bytes": (_SZ, [_I32, _I32]),
+    "mmsp_attn_packed_plan": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _VP, _SZ, _VP]),
     "mmsp_ring_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
                                          _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
     "mmsp_ring_backward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
@@ -133,6 +136,10 @@ def _need(t, dtype, name, ndim=None):
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
     del torch
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _shape(t, shape, name):
@@ -263,15 +270,43 @@ def shard_scatter(x, rows, out):
 
 
 # ---------------------------------------------------------------- a2
+def packed_plan(q_pos, q_start, k_pos, plan=None):
+    """Tile plan of the packed attention calls for these positions (int32
+    tensor of ``mmsp_attn_packed_plan_bytes`` bytes, on the positions' device):
+    every tile of the forward, dQ and dK/dV kernels listed heaviest first.
+    Scheduling only: ``attn_fwd_chunk`` / ``attn_bwd_chunk`` give the same
+    results with or without it.  ``plan`` may be given to reuse a buffer."""
+    import torch
+    _need(q_pos, torch.int32, "q_pos", 1)
+    _need(q_start, torch.int32, "q_start", 1)
+    _need(k_pos, torch.int32, "k_pos", 1)
+    sq, sk = q_pos.numel(), k_pos.numel()
+    if q_start.numel() != sq:
+        raise ValueError("q_start must have sq entries")
+    nbytes = lib().mmsp_attn_packed_plan_bytes(sq, sk)
+    if nbytes == 0:
+        raise ValueError("positions must not be empty")
+    if plan is None:
+        plan = torch.empty(nbytes // 4, dtype=torch.int32, device=q_pos.device)
+    _need(plan, torch.int32, "plan", 1)
+    _check(lib().mmsp_attn_packed_plan(_ptr(q_pos), _ptr(q_start), _ptr(k_pos), sq, sk,
+                                       _ptr(plan), plan.numel() * 4, _stream()),
+           "mmsp_attn_packed_plan")
+    return plan
+
+
 def attn_fwd_chunk(q, k, v, q_pos=None, k_pos=None, scale=None, causal=True, o=None, lse=None,
-                   accumulate=False, q_start=None):
+                   accumulate=False, q_start=None, plan=None):
     """Attention of ``q[sq,hq,d]`` against one chunk ``k, v[sk,hkv,d]`` (bf16).
 
     Returns ``(o fp32[sq,hq,d], lse fp32[hq,sq])``; with ``accumulate`` the
     given ``(o, lse)`` are merged with this chunk's result in place.
     ``q_start`` (int32[sq], optional): first position of each query's packed
     sample (reset attention masks between samples; needs ``causal``).
+    ``plan`` (optional, packed only): tile order from :func:`packed_plan`.
     """
+    if plan is not None and q_start is None:
+        raise ValueError("a tile plan applies to packed samples only")
     import torch
     _need(q, torch.bfloat16, "q", 3)
     _need(k, torch.bfloat16, "k", 3)
@@ -305,10 +340,11 @@ def attn_fwd_chunk(q, k, v, q_pos=None, k_pos=None, scale=None, causal=True, o=N
         _need(q_start, torch.int32, "q_start", 1)
         if q_start.numel() != sq:
             raise ValueError("q_start must have sq entries")
+        _need(plan, torch.int32, "plan", 1)
         _check(lib().mmsp_attn_fwd_chunk_packed(
             _ptr(q), _ptr(k), _ptr(v), _ptr(q_pos if causal else None), _ptr(q_start),
-            _ptr(k_pos if causal else None), sq, sk, hq, hkv, d, float(scale), flags, _ptr(o),
-            _ptr(lse), _stream()), "mmsp_attn_fwd_chunk_packed")
+            _ptr(k_pos if causal else None), _ptr(plan), _nbytes(plan), sq, sk, hq, hkv, d,
+            float(scale), flags, _ptr(o), _ptr(lse), _stream()), "mmsp_attn_fwd_chunk_packed")
         return o, lse
     _check(lib().mmsp_attn_fwd_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(q_pos if causal else None),
                                      _ptr(k_pos if causal else None), sq, sk, hq, hkv, d,
@@ -366,13 +402,16 @@ def attn_bwd_preprocess(o, dout, delta=None, dq_zero=None):
 
 # ---------------------------------------------------------------- a6
 def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=None,
-                   scale=None, causal=True, accumulate=False, q_start=None, part="both"):
+                   scale=None, causal=True, accumulate=False, q_start=None, part="both",
+                   plan=None):
     """Backward of one chunk: adds to ``dq_acc``; returns ``(dk, dv)`` fp32.
-    ``q_start`` as in :func:`attn_fwd_chunk`.  ``part`` = ``"dkdv"`` or ``"dq"``
+    ``q_start`` and ``plan`` as in :func:`attn_fwd_chunk`.  ``part`` = ``"dkdv"`` or ``"dq"``
     enqueues only that kernel (``dq_acc``, or ``dk``/``dv``, unused), so the
     two halves can run on two streams."""
     if part not in ("both", "dkdv", "dq"):
         raise ValueError("part must be 'both', 'dkdv' or 'dq'")
+    if plan is not None and q_start is None:
+        raise ValueError("a tile plan applies to packed samples only")
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, torch.bfloat16, n, 3)
@@ -415,11 +454,12 @@ def attn_bwd_chunk(q, k, v, dout, lse, delta, q_pos, k_pos, dq_acc, dk=None, dv=
         _need(q_start, torch.int32, "q_start", 1)
         if q_start.numel() != sq:
             raise ValueError("q_start must have sq entries")
+        _need(plan, torch.int32, "plan", 1)
         _check(lib().mmsp_attn_bwd_chunk_packed(
             _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
-            _ptr(q_pos if causal else None), _ptr(q_start), _ptr(k_pos if causal else None), sq,
-            sk, hq, hkv, d, float(scale), flags, _ptr(dq_acc), _ptr(dk), _ptr(dv), _stream()),
-            "mmsp_attn_bwd_chunk_packed")
+            _ptr(q_pos if causal else None), _ptr(q_start), _ptr(k_pos if causal else None),
+            _ptr(plan), _nbytes(plan), sq, sk, hq, hkv, d, float(scale), flags, _ptr(dq_acc),
+            _ptr(dk), _ptr(dv), _stream()), "mmsp_attn_bwd_chunk_packed")
         return dk, dv
     _check(lib().mmsp_attn_bwd_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
                                      _ptr(delta), _ptr(q_pos if causal else None),

@@ -24,34 +24,54 @@ def ring_order(rank: int, n_chunks: int):
     return [(rank - t) % n_chunks for t in range(n_chunks)]
 
 
+def packed_plans(q_pos, q_start, k_pos_chunks, plans=None):
+    """Tile plans of every chunk for packed samples (:func:`mmsp.packed_plan`),
+    indexed by chunk; one list serves the forward and the backward of a step.
+    ``plans`` may hold earlier plans whose buffers are reused."""
+    return [mmsp.packed_plan(q_pos, q_start, kp, plan=None if plans is None else plans[c])
+            for c, kp in enumerate(k_pos_chunks)]
+
+
+def _plans_for(q_pos, q_start, k_pos_chunks, causal, plans):
+    """The given plans, or new ones for packed samples, or none."""
+    if q_start is None or not causal:
+        return None
+    return plans if plans is not None else packed_plans(q_pos, q_start, k_pos_chunks)
+
+
 def ring_forward(q, k_chunks, v_chunks, q_pos, k_pos_chunks, rank=0, fused=True, scale=None,
                  causal=True, order=None, o_final=None, o=None, lse=None, timer=None,
-                 q_start=None):
+                 q_start=None, plans=None):
     """Forward over all chunks in ring order.
 
     Returns ``(o_acc fp32[sq,hq,d], lse fp32[hq,sq], o_bf16[sq,hq,d])``.  ``o``,
     ``lse`` and ``o_final`` may be given to reuse buffers; ``timer`` (optional)
     gets ``start/stop(kind, chunk)`` calls around every chunk launch.
-    ``q_start`` (optional): per-query sample starts of packed samples.
+    ``q_start`` (optional): per-query sample starts of packed samples;
+    ``plans`` (optional, per chunk) their tile plans (:func:`packed_plans`,
+    made here when not given).
     """
     import torch
     n = len(k_chunks)
     order = ring_order(rank, n) if order is None else order
+    plans = _plans_for(q_pos, q_start, k_pos_chunks, causal, plans)
     o_part = lse_part = None
     for step, c in enumerate(order):
         kp = k_pos_chunks[c] if causal else None
+        pl = None if plans is None else plans[c]
         if timer is not None:
             timer.start("fwd", c)
         if step == 0:
             o, lse = mmsp.attn_fwd_chunk(q, k_chunks[c], v_chunks[c], q_pos, kp, scale=scale,
-                                         causal=causal, o=o, lse=lse, q_start=q_start)
+                                         causal=causal, o=o, lse=lse, q_start=q_start, plan=pl)
         elif fused:
             mmsp.attn_fwd_chunk(q, k_chunks[c], v_chunks[c], q_pos, kp, scale=scale,
-                                causal=causal, o=o, lse=lse, accumulate=True, q_start=q_start)
+                                causal=causal, o=o, lse=lse, accumulate=True, q_start=q_start,
+                                plan=pl)
         else:
             o_part, lse_part = mmsp.attn_fwd_chunk(q, k_chunks[c], v_chunks[c], q_pos, kp,
                                                    scale=scale, causal=causal, o=o_part,
-                                                   lse=lse_part, q_start=q_start)
+                                                   lse=lse_part, q_start=q_start, plan=pl)
             mmsp.lse_merge(o, lse, o_part, lse_part)
         if timer is not None:
             timer.stop("fwd", c)
@@ -63,14 +83,16 @@ def ring_forward(q, k_chunks, v_chunks, q_pos, k_pos_chunks, rank=0, fused=True,
 
 def ring_backward(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks, rank=0,
                   scale=None, causal=True, order=None, dq=None, dks=None, dvs=None, delta=None,
-                  timer=None, q_start=None):
+                  timer=None, q_start=None, plans=None):
     """Backward over all chunks in ring order from the saved output and LSE.
 
     Returns ``(dq fp32[sq,hq,d], [dk_c fp32], [dv_c fp32])`` indexed by chunk.
+    ``q_start`` and ``plans`` as in :func:`ring_forward`.
     """
     import torch
     n = len(k_chunks)
     order = ring_order(rank, n) if order is None else order
+    plans = _plans_for(q_pos, q_start, k_pos_chunks, causal, plans)
     if dq is None:
         dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     delta = mmsp.attn_bwd_preprocess(o_bf16, dout, delta, dq_zero=dq)
@@ -82,7 +104,8 @@ def ring_backward(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks,
             timer.start("bwd", c)
         dks[c], dvs[c] = mmsp.attn_bwd_chunk(q, k_chunks[c], v_chunks[c], dout, lse, delta, q_pos,
                                              kp, dq, dk=dks[c], dv=dvs[c], scale=scale,
-                                             causal=causal, q_start=q_start)
+                                             causal=causal, q_start=q_start,
+                                             plan=None if plans is None else plans[c])
         if timer is not None:
             timer.stop("bwd", c)
     return dq, dks, dvs
@@ -174,13 +197,14 @@ class ChunkReceiver:
 
 def ring_forward_received(q, k_chunks, v_chunks, q_pos, k_pos_chunks, receiver, rank=0,
                           fused=True, scale=None, causal=True, o_final=None, o=None, lse=None,
-                          timer=None, q_start=None):
+                          timer=None, q_start=None, plans=None):
     """``ring_forward`` in ring order, with every chunk after the rank's own
     arriving through ``receiver`` (a :class:`ChunkReceiver`) while the previous
     chunk is computed.  Same kernels and order, so the same results."""
     import torch
     n = len(k_chunks)
     order = ring_order(rank, n)
+    plans = _plans_for(q_pos, q_start, k_pos_chunks, causal, plans)
     o_part = lse_part = None
     receiver.start()
     for step, c in enumerate(order):
@@ -191,18 +215,19 @@ def ring_forward_received(q, k_chunks, v_chunks, q_pos, k_pos_chunks, receiver, 
         if step + 1 < n:  # the next chunk arrives while this one is computed
             receiver.receive(step + 1, k_chunks[order[step + 1]], v_chunks[order[step + 1]])
         kp = k_pos_chunks[c] if causal else None
+        pl = None if plans is None else plans[c]
         if timer is not None:
             timer.start("fwd", c)
         if step == 0:
             o, lse = mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale, causal=causal, o=o,
-                                         lse=lse, q_start=q_start)
+                                         lse=lse, q_start=q_start, plan=pl)
         elif fused:
             mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale, causal=causal, o=o, lse=lse,
-                                accumulate=True, q_start=q_start)
+                                accumulate=True, q_start=q_start, plan=pl)
         else:
             o_part, lse_part = mmsp.attn_fwd_chunk(q, kc, vc, q_pos, kp, scale=scale,
                                                    causal=causal, o=o_part, lse=lse_part,
-                                                   q_start=q_start)
+                                                   q_start=q_start, plan=pl)
             mmsp.lse_merge(o, lse, o_part, lse_part)
         if timer is not None:
             timer.stop("fwd", c)
@@ -218,13 +243,14 @@ def ring_forward_received(q, k_chunks, v_chunks, q_pos, k_pos_chunks, receiver, 
 def ring_backward_received(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_pos_chunks,
                            receiver, rank=0, scale=None, causal=True, dq=None, dks=None,
                            dvs=None, dk_sent=None, dv_sent=None, delta=None, timer=None,
-                           q_start=None):
+                           q_start=None, plans=None):
     """``ring_backward`` with chunks arriving through ``receiver`` and each
     chunk's dK/dV sent (copied to ``dk_sent[c]``/``dv_sent[c]``) on the copy
     stream as soon as they are computed."""
     import torch
     n = len(k_chunks)
     order = ring_order(rank, n)
+    plans = _plans_for(q_pos, q_start, k_pos_chunks, causal, plans)
     if dq is None:
         dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     receiver.start()
@@ -243,7 +269,8 @@ def ring_backward_received(q, k_chunks, v_chunks, dout, o_bf16, lse, q_pos, k_po
             timer.start("bwd", c)
         dks[c], dvs[c] = mmsp.attn_bwd_chunk(q, kc, vc, dout, lse, delta, q_pos, kp, dq,
                                              dk=dks[c], dv=dvs[c], scale=scale, causal=causal,
-                                             q_start=q_start)
+                                             q_start=q_start,
+                                             plan=None if plans is None else plans[c])
         if timer is not None:
             timer.stop("bwd", c)
         if step > 0:

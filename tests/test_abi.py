@@ -124,24 +124,24 @@ def test_binding_raises_with_code():
 
 
 def fwd_packed(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, qp=FAKE, qs=FAKE, kp=FAKE, sq=128, sk=128, hq=4, hkv=2,
-             d=128, scale=0.088, flags=1, o=FAKE, lse=FAKE)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qp=FAKE, qs=FAKE, kp=FAKE, plan=None, plan_bytes=0, sq=128,
+             sk=128, hq=4, hkv=2, d=128, scale=0.088, flags=1, o=FAKE, lse=FAKE)
     a.update(kw)
     return mmsp.lib().mmsp_attn_fwd_chunk_packed(a["q"], a["k"], a["v"], a["qp"], a["qs"],
-                                                 a["kp"], a["sq"], a["sk"], a["hq"], a["hkv"],
-                                                 a["d"], a["scale"], a["flags"], a["o"],
-                                                 a["lse"], None)
+                                                 a["kp"], a["plan"], a["plan_bytes"], a["sq"],
+                                                 a["sk"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                                 a["flags"], a["o"], a["lse"], None)
 
 
 def bwd_packed(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, lse=FAKE, delta=FAKE, qp=FAKE, qs=FAKE, kp=FAKE,
-             sq=128, sk=128, hq=4, hkv=2, d=64, scale=0.125, flags=1, dq=FAKE, dk=FAKE,
-             dv=FAKE)
+             plan=None, plan_bytes=0, sq=128, sk=128, hq=4, hkv=2, d=64, scale=0.125, flags=1,
+             dq=FAKE, dk=FAKE, dv=FAKE)
     a.update(kw)
     return mmsp.lib().mmsp_attn_bwd_chunk_packed(
         a["q"], a["k"], a["v"], a["do"], a["lse"], a["delta"], a["qp"], a["qs"], a["kp"],
-        a["sq"], a["sk"], a["hq"], a["hkv"], a["d"], a["scale"], a["flags"], a["dq"], a["dk"],
-        a["dv"], None)
+        a["plan"], a["plan_bytes"], a["sq"], a["sk"], a["hq"], a["hkv"], a["d"], a["scale"],
+        a["flags"], a["dq"], a["dk"], a["dv"], None)
 
 
 @pytest.mark.parametrize("fn", [fwd_packed, bwd_packed])
@@ -149,9 +149,41 @@ def bwd_packed(**kw):
     (dict(qs=None), -1), (dict(flags=0), -3), (dict(flags=2), -3), (dict(qp=None), -1),
     (dict(q=None), -1), (dict(sq=0), -2), (dict(d=80), -3), (dict(hq=5, hkv=2), -4),
     (dict(flags=17), -3),  # an undefined bit
+    (dict(plan=FAKE, plan_bytes=0), -5), (dict(plan=FAKE, plan_bytes=40), -5),  # plan too small
+    (dict(plan=FAKE, plan_bytes=1 << 20, sq=0), -2),
 ])
 def test_packed_attention_rejects(fn, kw, code):
     assert fn(**kw) == code
+
+
+def test_packed_plan_size_and_rejects():
+    lib = mmsp.lib()
+    nb = lib.mmsp_attn_packed_plan_bytes
+    # header of 8 words, then a list and a work count per tile: forward tiles of
+    # 256 query rows, dQ tiles of 128, dK/dV tiles of 128 keys
+    assert nb(8192, 8192) == 4 * (8 + 2 * (32 + 64 + 64))
+    assert nb(1, 1) == 4 * (8 + 2 * 3)
+    assert nb(257, 129) == 4 * (8 + 2 * (2 + 3 + 2))
+    assert nb(0, 16) == 0 and nb(16, -1) == 0
+    f = lib.mmsp_attn_packed_plan
+    need = nb(128, 128)
+    assert f(None, FAKE, FAKE, 128, 128, FAKE, need, None) == -1
+    assert f(FAKE, None, FAKE, 128, 128, FAKE, need, None) == -1
+    assert f(FAKE, FAKE, None, 128, 128, FAKE, need, None) == -1
+    assert f(FAKE, FAKE, FAKE, 128, 128, None, need, None) == -1
+    assert f(FAKE, FAKE, FAKE, 0, 128, FAKE, need, None) == -2
+    assert f(FAKE, FAKE, FAKE, 128, 0, FAKE, need, None) == -2
+    assert f(FAKE, FAKE, FAKE, 128, 128, FAKE, need - 4, None) == -5
+
+
+def test_plan_rejected_without_packed_samples():
+    import torch
+    q = torch.zeros(4, 1, 64, dtype=torch.bfloat16)
+    plan = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mmsp.attn_fwd_chunk(q, q, q, causal=False, plan=plan)
+    with pytest.raises(ValueError):
+        mmsp.attn_bwd_chunk(q, q, q, q, None, None, None, None, None, causal=False, plan=plan)
 
 
 def test_packed_shard_balance_rejects():

@@ -135,3 +135,118 @@ def test_packed_single_sample_equals_plain_causal(mm):
     assert torch.equal(ga[0], gb_[0])
     for c in range(2):
         assert torch.equal(ga[1][c], gb_[1][c]) and torch.equal(ga[2][c], gb_[2][c])
+
+
+# Tile shapes of the kernels the plan orders (scheduling, not the method):
+# forward workgroups of 256 query rows over 64-key tiles, dQ workgroups of 128
+# rows over 64-key tiles, dK/dV workgroups of 128 keys over 32-row tiles.
+_FWD_BM, _FWD_BN, _DQ_BM, _DQ_BN, _KV_BK, _KV_BQ = 256, 64, 128, 64, 128, 32
+
+
+def _expected_plan(qp, qs, kp):
+    """Header, heaviest-first tile lists and work counts of a tile plan,
+    counted directly from the positions (ties in ascending tile order)."""
+    sq, sk = qp.size, kp.size
+
+    def qtiles(bm, bn):
+        w = []
+        for q0 in range(0, sq, bm):
+            qmax = qp[min(q0 + bm, sq) - 1]
+            nk = np.searchsorted(kp, qmax, side="right")
+            kbeg = np.searchsorted(kp, qs[q0], side="left")
+            w.append(max(0, -(-nk // bn) - kbeg // bn))
+        return np.array(w, dtype=np.int64)
+
+    def ktiles():
+        w = []
+        for j0 in range(0, sk, _KV_BK):
+            kk = kp[j0:j0 + _KV_BK]
+            qbeg = np.searchsorted(qp, kk[0], side="left")
+            qend = np.searchsorted(qs, kk[-1], side="right")
+            w.append(max(0, -(-qend // _KV_BQ) - qbeg // _KV_BQ))
+        return np.array(w, dtype=np.int64)
+
+    works = [qtiles(_FWD_BM, _FWD_BN), qtiles(_DQ_BM, _DQ_BN), ktiles()]
+    lists = [np.lexsort((np.arange(w.size), -w)) for w in works]
+    header = [0x4E414C50, sq, sk] + [w.size for w in works] + [0, 0]
+    return np.concatenate([header] + lists + works).astype(np.int32)
+
+
+def _plan_cases():
+    cases = []
+    for lens, p, rank in (([1024, 512, 2048, 512], 2, 0), ([100, 60, 200, 44], 2, 1),
+                          ([32] * 20 + [640], 4, 3)):
+        starts = np.concatenate([[0], np.cumsum(lens)])
+        perm, first = oracle.zigzag_packed_perm(starts, p)
+        shard = perm.size // p
+        qp, qs = perm[rank * shard:(rank + 1) * shard], first[rank * shard:(rank + 1) * shard]
+        for c in range(p):
+            cases.append((qp, qs, perm[c * shard:(c + 1) * shard]))
+    return cases
+
+
+def test_packed_plan_lists_tiles_heaviest_first(mm):
+    """Bit-exact plan on small shards and on every chunk of the 65,536-token
+    packed workload's rank 0 (5 clips, per-sample zigzag over 8 ranks)."""
+    mmsp, ring = mm
+    from long_context_multimodal_amd import workloads as W
+    cases = _plan_cases()
+    w = W.PACKED_TRAIN
+    perm, first = oracle.zigzag_packed_perm(w.sample_starts(), w.n_ranks)
+    for c in range(w.n_chunks):
+        cases.append((perm[:w.shard], first[:w.shard], perm[c * w.chunk:(c + 1) * w.chunk]))
+    for i, (qp, qs, kp) in enumerate(cases):
+        want = _expected_plan(qp, qs, kp)
+        got = to_np(mmsp.packed_plan(to_dev_i32(qp), to_dev_i32(qs), to_dev_i32(kp)))
+        assert got.size == want.size, i
+        assert np.array_equal(got, want), f"case {i}"
+        n = want[3:6]
+        lists = np.split(want[8:8 + n.sum()], np.cumsum(n)[:2])
+        for lst, m in zip(lists, n):  # every tile exactly once
+            assert sorted(lst.tolist()) == list(range(m))
+
+
+@pytest.mark.parametrize("lens,p,rank,hq,hkv,d", [
+    ([1024, 512, 2048, 512], 2, 0, 8, 8, 128),  # 8 heads: each XCD keeps its own head
+    ([1024, 512, 2048, 512], 2, 1, 4, 2, 64),   # heads simply take turns
+    ([100, 60, 200, 44], 2, 1, 7, 1, 128),      # ragged shard, GQA 7
+])
+def test_packed_plan_leaves_results_unchanged(mm, lens, p, rank, hq, hkv, d):
+    """A plan only reorders workgroups: forward and backward give the same
+    bits with the plan, without it, with a plan of other positions of the same
+    sizes, and with a plan of other sizes (which the kernels ignore)."""
+    mmsp, ring = mm
+    import torch
+    qp, qs, kps, (qb, _), (kb, _), (vb, _), (gb, _) = _packed_ring_inputs(
+        lens, p, rank, hq, hkv, d, seed=90 + d)
+    q, do = to_dev_bf16(qb), to_dev_bf16(gb)
+    qp_d, qs_d = to_dev_i32(qp), to_dev_i32(qs)
+    c = (rank + 1) % p  # a chunk of another rank
+    k, v, kp_d = to_dev_bf16(kb[c]), to_dev_bf16(vb[c]), to_dev_i32(kps[c])
+    sq, sk = qp.size, kps[c].size
+    plans = {
+        "none": None,
+        "own": mmsp.packed_plan(qp_d, qs_d, kp_d),
+        # the rank's own chunk: same sizes, other positions
+        "other positions": mmsp.packed_plan(qp_d, qs_d, to_dev_i32(kps[rank])),
+    }
+    # a plan made for fewer queries, in a buffer large enough for these sizes
+    small = mmsp.packed_plan(qp_d[:sq // 2].contiguous(), qs_d[:sq // 2].contiguous(), kp_d)
+    buf = torch.zeros(mmsp.lib().mmsp_attn_packed_plan_bytes(sq, sk) // 4, dtype=torch.int32,
+                      device=q.device)
+    buf[:small.numel()] = small
+    plans["other sizes"] = buf
+    outs = {}
+    for name, plan in plans.items():
+        o, lse = mmsp.attn_fwd_chunk(q, k, v, qp_d, kp_d, q_start=qs_d, plan=plan)
+        o16 = torch.empty(o.shape, dtype=torch.bfloat16, device=o.device)
+        mmsp.lse_merge(o, lse, None, None, o_final=o16)
+        delta = mmsp.attn_bwd_preprocess(o16, do)
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+        dk, dv = mmsp.attn_bwd_chunk(q, k, v, do, lse, delta, qp_d, kp_d, dq, q_start=qs_d,
+                                     plan=plan)
+        outs[name] = (o, lse, dq, dk, dv)
+    torch.cuda.synchronize()
+    for name, got in outs.items():
+        for x, y, what in zip(outs["none"], got, ("O", "LSE", "dQ", "dK", "dV")):
+            assert torch.equal(x, y), f"{what} with plan '{name}'"
