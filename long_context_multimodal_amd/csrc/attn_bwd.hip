@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   wkmin = uniform(wkmin);
   wkmax = uniform(wkmax);
   int qstart = 0;
-  if (p.causal) {
+  if (p.causal && !PACKED) {
     const int kmin = p.k_pos[j0];
     int lo = 0, hi = p.sq;
     while (lo < hi) {
@@ -120,17 +120,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
     qstart = lo;
   }
   // packed samples: only queries whose sample starts at or before the
-  // workgroup's last key can see it (sample starts are non-decreasing)
+  // workgroup's last key can see it (sample starts are non-decreasing); both
+  // ends come from one wave-wide search (the plain instance keeps the binary
+  // search above: the wave-wide one pushes its registers past 256)
   constexpr bool packed = PACKED;  // q_start given
   int qend = p.sq;
   if (packed) {
-    const int kmax = p.k_pos[min(j0 + C::BK - 1, p.sk - 1)];
-    int lo = 0, hi = p.sq;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (p.q_start[mid] <= kmax) lo = mid + 1; else hi = mid;
-    }
-    qend = lo;
+    const int kmin = p.k_pos[j0], kmax = p.k_pos[min(j0 + C::BK - 1, p.sk - 1)];
+    wave_prefix_two<false, true>(p.q_pos, p.sq, kmin, p.q_start, p.sq, kmax, qstart, qend);
   }
   const int n_qt = uniform((qend + C::BQ - 1) / C::BQ);
   const int qt0 = qstart / C::BQ;
@@ -536,26 +533,15 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   const int wqs_min = uniform((packed && wave_live) ? p.q_start[wr0] : INT_MIN);
   const int wqs_max =
       uniform((packed && wave_live) ? p.q_start[min(wr0 + 31, p.sq - 1)] : INT_MIN);
-  // key range of the workgroup: [kbeg, nk)
-  int nk = p.sk;
+  // key range of the workgroup: [kbeg, nk) -- keys at or below its last
+  // position and, with packed samples, at or after its first sample start
+  int nk = p.sk, kbeg = 0;
   if (p.causal) {
     const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
-    int lo = 0, hi = p.sk;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (p.k_pos[mid] <= qmax) lo = mid + 1; else hi = mid;
-    }
-    nk = lo;
-  }
-  int kbeg = 0;
-  if (packed) {
-    const int qsmin = p.q_start[q0];
-    int lo = 0, hi = p.sk;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (p.k_pos[mid] < qsmin) lo = mid + 1; else hi = mid;
-    }
-    kbeg = lo;
+    if constexpr (packed)
+      wave_prefix_two<true, false>(p.k_pos, p.sk, qmax, p.k_pos, p.sk, p.q_start[q0], nk, kbeg);
+    else
+      nk = wave_prefix<true>(p.k_pos, p.sk, qmax);
   }
   const int tb = uniform(kbeg / C::BN);  // first tile
   const int nt = uniform(max(0, (nk + C::BN - 1) / C::BN - tb));

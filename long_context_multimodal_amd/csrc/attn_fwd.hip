@@ -146,26 +146,15 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     bqs_max[qb] = uniform((packed && r0 < p.sq) ? p.q_start[min(r0 + 31, p.sq - 1)] : INT_MIN);
   }
   const int wqs_min = uniform((packed && wave_live) ? p.q_start[wr0] : INT_MIN);
-  // key range of the workgroup: [kbeg, nk)
-  int nk = p.sk;
+  // key range of the workgroup: [kbeg, nk) -- keys at or below its last
+  // position and, with packed samples, at or after its first sample start
+  int nk = p.sk, kbeg = 0;
   if (p.causal) {
     const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
-    int lo = 0, hi = p.sk;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (p.k_pos[mid] <= qmax) lo = mid + 1; else hi = mid;
-    }
-    nk = lo;
-  }
-  int kbeg = 0;
-  if (packed) {
-    const int qsmin = p.q_start[q0];
-    int lo = 0, hi = p.sk;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (p.k_pos[mid] < qsmin) lo = mid + 1; else hi = mid;
-    }
-    kbeg = lo;
+    if constexpr (packed)
+      wave_prefix_two<true, false>(p.k_pos, p.sk, qmax, p.k_pos, p.sk, p.q_start[q0], nk, kbeg);
+    else
+      nk = wave_prefix<true>(p.k_pos, p.sk, qmax);
   }
   const int tb = uniform(kbeg / C::BN);  // first tile
   const int nt = uniform(max(0, (nk + C::BN - 1) / C::BN - tb));

@@ -112,6 +112,63 @@ __device__ __forceinline__ int heavy_first_tile(int i, int n, int grid) {
   return (blk << 3) | (i & 7);
 }
 
+// Lengths of the prefixes of two non-decreasing arrays on which a predicate
+// holds: a[i] < xa (or <= xa with LE_A) and b[i] < xb (or <= xb with LE_B).
+// Each round every lane of the wave probes one entry of each unresolved range
+// and a ballot finds where the predicate turns false, so a range shrinks
+// 64-fold per round: 8192 entries take three rounds (one load each, the two
+// searches side by side) instead of thirteen dependent loads.  Call with the
+// whole wave active; results are wave-uniform.
+template <bool LE_A, bool LE_B>
+__device__ __forceinline__ void wave_prefix_two(const int32_t* a, int na, int xa, const int32_t* b,
+                                                int nb, int xb, int& ca, int& cb) {
+  const int lane = (int)(threadIdx.x & 63);
+  int alo = 0, ahi = na, blo = 0, bhi = nb;
+  while (alo < ahi || blo < bhi) {
+    const int as = (ahi - alo + 63) >> 6, bs = (bhi - blo + 63) >> 6;
+    const int ai = alo + (lane + 1) * as - 1, bi = blo + (lane + 1) * bs - 1;
+    bool aok = false, bok = false;
+    if (as > 0 && ai < ahi) {  // a resolved range (as == 0) is not probed
+      const int v = a[ai];
+      aok = LE_A ? v <= xa : v < xa;
+    }
+    if (bs > 0 && bi < bhi) {
+      const int v = b[bi];
+      bok = LE_B ? v <= xb : v < xb;
+    }
+    // the predicate holds on a prefix of the probes: lanes [0, n)
+    const int an = __popcll(__ballot(aok)), bn = __popcll(__ballot(bok));
+    const int af = alo + (an + 1) * as - 1, bf = blo + (bn + 1) * bs - 1;  // first failing probe
+    ahi = uniform((as > 0 && an < 64 && af < ahi) ? af : ahi);
+    bhi = uniform((bs > 0 && bn < 64 && bf < bhi) ? bf : bhi);
+    alo = uniform(min(alo + an * as, ahi));
+    blo = uniform(min(blo + bn * bs, bhi));
+  }
+  ca = alo;
+  cb = blo;
+}
+
+// wave_prefix_two for one array.
+template <bool LE>
+__device__ __forceinline__ int wave_prefix(const int32_t* a, int n, int x) {
+  const int lane = (int)(threadIdx.x & 63);
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int st = (hi - lo + 63) >> 6;
+    const int i = lo + (lane + 1) * st - 1;
+    bool ok = false;
+    if (i < hi) {
+      const int v = a[i];
+      ok = LE ? v <= x : v < x;
+    }
+    const int k = __popcll(__ballot(ok));
+    const int f = lo + (k + 1) * st - 1;
+    hi = uniform((k < 64 && f < hi) ? f : hi);
+    lo = uniform(min(lo + k * st, hi));
+  }
+  return lo;
+}
+
 // Head and tile of workgroup b from a work-ordered tile list (heaviest first)
 // of n tiles per head, H heads.  As with xcd_logical_block, each XCD keeps a
 // contiguous share of the heads (with H a multiple of 8); within it the heads
