@@ -48,41 +48,106 @@ __device__ __forceinline__ void count_two(const int32_t* a, int xa, const int32_
   cb = pb;
 }
 
-// Work of every tile, in tiles of the kernel's inner loop: key tiles for the
-// query-stationary forward and dQ kernels (from the first key at or after the
-// tile's smallest sample start to the last key at or before its largest
-// position), query tiles for the key-stationary dK/dV kernel (from the first
-// query at or after the tile's smallest key position to the last query whose
-// sample starts at or before its largest one).
-__global__ void __launch_bounds__(256) plan_work_kernel(PlanArgs a) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= a.n_fwd + a.n_dq + a.n_dkdv) return;
-  int w;
+// Work of tile i (all three sections numbered together), in tiles of the
+// kernel's inner loop: key tiles for the query-stationary forward and dQ
+// kernels (from the first key at or after the tile's smallest sample start to
+// the last key at or before its largest position), query tiles for the
+// key-stationary dK/dV kernel (from the first query at or after the tile's
+// smallest key position to the last query whose sample starts at or before
+// its largest one).  The position arrays may sit in global memory or in LDS.
+__device__ __forceinline__ int tile_work(const PlanArgs& a, const int32_t* q_pos,
+                                         const int32_t* q_start, const int32_t* k_pos, int i) {
   if (i < a.n_fwd + a.n_dq) {
     const bool fwd = i < a.n_fwd;
     const int t = fwd ? i : i - a.n_fwd;
     const int bm = fwd ? a.fwd_bm : a.dq_bm, bn = fwd ? a.fwd_bn : a.dq_bn;
     const int q0 = t * bm;
-    const int qmax = a.q_pos[min(q0 + bm - 1, a.sq - 1)];
+    const int qmax = q_pos[min(q0 + bm - 1, a.sq - 1)];
     int kbeg, nk;
-    count_two(a.k_pos, a.q_start[q0], a.k_pos, qmax, a.sk, kbeg, nk);
-    w = max(0, (nk + bn - 1) / bn - kbeg / bn);
-  } else {
-    const int t = i - a.n_fwd - a.n_dq;
-    const int j0 = t * a.dkdv_bk;
-    const int kmin = a.k_pos[j0], kmax = a.k_pos[min(j0 + a.dkdv_bk - 1, a.sk - 1)];
-    int qbeg, qend;
-    count_two(a.q_pos, kmin, a.q_start, kmax, a.sq, qbeg, qend);
-    w = max(0, (qend + a.dkdv_bq - 1) / a.dkdv_bq - qbeg / a.dkdv_bq);
+    count_two(k_pos, q_start[q0], k_pos, qmax, a.sk, kbeg, nk);
+    return max(0, (nk + bn - 1) / bn - kbeg / bn);
   }
-  a.plan[a.work_off + i] = w;
+  const int t = i - a.n_fwd - a.n_dq;
+  const int j0 = t * a.dkdv_bk;
+  const int kmin = k_pos[j0], kmax = k_pos[min(j0 + a.dkdv_bk - 1, a.sk - 1)];
+  int qbeg, qend;
+  count_two(q_pos, kmin, q_start, kmax, a.sq, qbeg, qend);
+  return max(0, (qend + a.dkdv_bq - 1) / a.dkdv_bq - qbeg / a.dkdv_bq);
+}
+
+__device__ __forceinline__ void write_header(const PlanArgs& a) {
+  a.plan[0] = kPlanMagic;
+  a.plan[1] = a.sq;
+  a.plan[2] = a.sk;
+  a.plan[3] = a.n_fwd;
+  a.plan[4] = a.n_dq;
+  a.plan[5] = a.n_dkdv;
+  a.plan[6] = 0;
+  a.plan[7] = 0;
+}
+
+// Shards of at most kSmallPlan positions (the usual case): one workgroup
+// stages the three position arrays in LDS, counts every tile's work there and
+// ranks the tiles, in one launch.
+constexpr int kSmallPlan = 8192;
+constexpr int kSmallThreads = 1024;
+
+__global__ void __launch_bounds__(kSmallThreads) plan_small_kernel(PlanArgs a) {
+  __shared__ int32_t s_q[kSmallPlan], s_s[kSmallPlan], s_k[kSmallPlan];
+  __shared__ int32_t s_w[kSmallThreads];
+  const int tid = threadIdx.x;
+  // every load issued before the first store: one memory round trip
+  constexpr int PER = kSmallPlan / kSmallThreads;
+  int32_t rk[PER], rq[PER], rs[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * kSmallThreads;
+    rk[u] = i < a.sk ? a.k_pos[i] : 0;
+    rq[u] = i < a.sq ? a.q_pos[i] : 0;
+    rs[u] = i < a.sq ? a.q_start[i] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * kSmallThreads;
+    s_k[i] = rk[u];
+    s_q[i] = rq[u];
+    s_s[i] = rs[u];
+  }
+  __syncthreads();
+  const int total = a.n_fwd + a.n_dq + a.n_dkdv;  // <= kSmallThreads for these sizes
+  const int w = tid < total ? tile_work(a, s_q, s_s, s_k, tid) : -1;
+  s_w[tid] = w;
+  __syncthreads();
+  if (tid < total) {
+    a.plan[a.work_off + tid] = w;
+    // rank within the section: descending work, ties by ascending index
+    const int sec = tid < a.n_fwd ? 0 : tid < a.n_fwd + a.n_dq ? 1 : 2;
+    const int b = sec == 0 ? 0 : sec == 1 ? a.n_fwd : a.n_fwd + a.n_dq;
+    const int n = sec == 0 ? a.n_fwd : sec == 1 ? a.n_dq : a.n_dkdv;
+    const int list = sec == 0 ? a.fwd_off : sec == 1 ? a.dq_off : a.dkdv_off;
+    int rank = 0;
+    for (int j = b; j < b + n; ++j) {
+      const int wj = s_w[j];
+      rank += (wj > w) || (wj == w && j < tid);
+    }
+    a.plan[list + rank] = tid - b;
+  }
+  if (tid == 0) write_header(a);
+}
+
+// Larger shards: one thread per tile counts its work from global memory ...
+__global__ void __launch_bounds__(256) plan_work_kernel(PlanArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.n_fwd + a.n_dq + a.n_dkdv) return;
+  a.plan[a.work_off + i] = tile_work(a, a.q_pos, a.q_start, a.k_pos, i);
 }
 
 // Sections longer than this keep index order: ranking costs n^2 compares.
 constexpr int kMaxRanked = 1 << 15;
 
-// One thread per tile of section blockIdx.y: its rank among the section's
-// tiles by descending work, ties by ascending index, is its slot in the list.
+// ... then one thread per tile of section blockIdx.y finds its rank among the
+// section's tiles by descending work, ties by ascending index: its slot in
+// the list.
 __global__ void __launch_bounds__(256) plan_order_kernel(PlanArgs a) {
   __shared__ int sw[256];
   const int sec = blockIdx.y;
@@ -109,16 +174,7 @@ __global__ void __launch_bounds__(256) plan_order_kernel(PlanArgs a) {
     }
     if (i < n) a.plan[list + rank] = i;
   }
-  if (sec == 0 && i == 0) {
-    a.plan[0] = kPlanMagic;
-    a.plan[1] = a.sq;
-    a.plan[2] = a.sk;
-    a.plan[3] = a.n_fwd;
-    a.plan[4] = a.n_dq;
-    a.plan[5] = a.n_dkdv;
-    a.plan[6] = 0;
-    a.plan[7] = 0;
-  }
+  if (sec == 0 && i == 0) write_header(a);
 }
 
 }  // namespace
@@ -152,6 +208,10 @@ hipError_t launch_tile_plan(const int32_t* q_pos, const int32_t* q_start, const 
   a.work_off = s.work_off();
   a.plan = plan;
   const int total = s.n_fwd + s.n_dq + s.n_dkdv;
+  if (sq <= kSmallPlan && sk <= kSmallPlan && total <= kSmallThreads) {
+    hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(plan_work_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

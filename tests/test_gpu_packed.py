@@ -174,8 +174,10 @@ def _expected_plan(qp, qs, kp):
 
 def _plan_cases():
     cases = []
+    # shards up to 8192 positions take the one-workgroup plan; the last case
+    # (16384-row shard) the two-kernel plan for larger shards
     for lens, p, rank in (([1024, 512, 2048, 512], 2, 0), ([100, 60, 200, 44], 2, 1),
-                          ([32] * 20 + [640], 4, 3)):
+                          ([32] * 20 + [640], 4, 3), ([8192, 4100, 12284, 8192], 2, 1)):
         starts = np.concatenate([[0], np.cumsum(lens)])
         perm, first = oracle.zigzag_packed_perm(starts, p)
         shard = perm.size // p
