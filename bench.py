@@ -320,6 +320,34 @@ def sdpa_context(torch, w, iters, device):
         return {"skipped": f"{type(e).__name__}: {str(e)[:200]}"}
 
 
+def gemm_context(torch, iters, device, n=8192):
+    """A library bf16 GEMM (torch.matmul, n x n x n, fp32 accumulate) run back
+    to back: how much of the nominal MFMA peak a plain dense contraction
+    sustains on the box (its clock under load is in the clock counters),
+    timed for comparison only."""
+    try:
+        a = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+        c = torch.empty(n, n, device=device, dtype=torch.bfloat16)
+        reps = max(iters, 50)
+        for _ in range(5):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        return {"what": f"torch.matmul bf16 [{n}, {n}] x [{n}, {n}], {reps} calls back to back",
+                "torch": torch.__version__, "ms": round(ms, 4),
+                "tflops": round(2.0 * n ** 3 / ms / 1e9, 1),
+                "pct_of_peak": round(100 * 2.0 * n ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    except Exception as e:  # context only
+        return {"skipped": f"{type(e).__name__}: {str(e)[:200]}"}
+
+
 def device_record(torch, mmsp):
     """What the run was on: the peak the roofline uses is the published one
     (2.4 GHz); the clock the runtime reports and the one reached under load
@@ -368,6 +396,9 @@ def main():
     ap.add_argument("--native-ring", action="store_true",
                     help="also time the step with the ring loop in the library (mmsp_ring_forward "
                          "/ mmsp_ring_backward) and check its outputs against the Python driver's")
+    ap.add_argument("--gemm-context", action="store_true",
+                    help="also time a library bf16 GEMM (torch.matmul, 8192^3) back to back: the dense "
+                         "MFMA rate the box sustains, for comparison only")
     ap.add_argument("--no-plan", action="store_true",
                     help="packed samples: keep the kernels' built-in tile order instead of the "
                          "work-ordered tile plan made each step")
@@ -689,6 +720,8 @@ def main():
         del stream, into
     if args.sdpa_context:
         result["sdpa_context"] = sdpa_context(torch, w, args.steps, device)
+    if args.gemm_context:
+        result["gemm_context"] = gemm_context(torch, args.steps, device)
     if args.native_ring:
         outs = [o, lse, o16] + ([dq] + dks + dvs if w.backward else [])
 
