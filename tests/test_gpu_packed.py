@@ -176,8 +176,9 @@ def _plan_cases():
     cases = []
     # shards up to 8192 positions take the one-workgroup plan; the last case
     # (16384-row shard) the two-kernel plan for larger shards
-    for lens, p, rank in (([1024, 512, 2048, 512], 2, 0), ([100, 60, 200, 44], 2, 1),
-                          ([32] * 20 + [640], 4, 3), ([8192, 4100, 12284, 8192], 2, 1)):
+    for lens, p, rank in (([2], 1, 0), ([4, 8], 2, 1), ([1024, 512, 2048, 512], 2, 0),
+                          ([100, 60, 200, 44], 2, 1), ([32] * 20 + [640], 4, 3),
+                          ([8192, 4100, 12284, 8192], 2, 1)):
         starts = np.concatenate([[0], np.cumsum(lens)])
         perm, first = oracle.zigzag_packed_perm(starts, p)
         shard = perm.size // p
@@ -209,6 +210,7 @@ def test_packed_plan_lists_tiles_heaviest_first(mm):
 
 
 @pytest.mark.parametrize("lens,p,rank,hq,hkv,d", [
+    ([4, 8], 2, 1, 2, 1, 64),                   # 6-row shard: one tile in every list
     ([1024, 512, 2048, 512], 2, 0, 8, 8, 128),  # 8 heads: each XCD keeps its own head
     ([1024, 512, 2048, 512], 2, 1, 4, 2, 64),   # heads simply take turns
     ([100, 60, 200, 44], 2, 1, 7, 1, 128),      # ragged shard, GQA 7
