@@ -637,23 +637,20 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
         f32x16 dinit;
 #pragma unroll
         for (int i = 0; i < 16; ++i) dinit[i] = -delta;  // dP accumulates onto -delta
-        // K / V operands read two contractions ahead of their use (S and dP
-        // alternate); a scheduling barrier after every contraction holds that
-        // order, which the scheduler otherwise folds back to read, wait, MFMA
+        // S first, its K operands read two contractions ahead; then dP, its V
+        // operands likewise, with two of the exponentials of S after each of
+        // its contractions; a scheduling barrier after every group holds the
+        // order (otherwise the scheduler folds the reads back to read, wait,
+        // MFMA and the exponentials after the last contraction)
         constexpr int LA = 2;
-        bf16x8 op[2 * C::KS];
-        auto rd = [&](int i) { return lds_read_b128((i & 1) ? vt : kt, rb + koff[i >> 1]); };
+        bf16x8 op[C::KS];
 #pragma unroll
-        for (int i = 0; i < LA; ++i) op[i] = rd(i);
+        for (int i = 0; i < LA; ++i) op[i] = lds_read_b128(kt, rb + koff[i]);
         f32x16 s = f32x16{};
-        f32x16 dp = dinit;
 #pragma unroll
-        for (int i = 0; i < 2 * C::KS; ++i) {
-          if (i + LA < 2 * C::KS) op[i + LA] = rd(i + LA);
-          if (i & 1)
-            dp = mfma32x32x16(op[i], df[i >> 1], dp);
-          else
-            s = mfma32x32x16(op[i], qf[i >> 1], s);
+        for (int i = 0; i < C::KS; ++i) {
+          if (i + LA < C::KS) op[i + LA] = lds_read_b128(kt, rb + koff[i + LA]);
+          s = mfma32x32x16(op[i], qf[i], s);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (straddle) {
@@ -668,13 +665,23 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
               s[i] = (kp[key] > qpos) ? -INFINITY : s[i];
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < LA; ++i) op[i] = lds_read_b128(vt, rb + koff[i]);
+        f32x16 dp = dinit;
+        constexpr int EPM = 16 / C::KS;  // exponentials per contraction
+#pragma unroll
+        for (int i = 0; i < C::KS; ++i) {
+          if (i + LA < C::KS) op[i + LA] = lds_read_b128(vt, rb + koff[i + LA]);
+          dp = mfma32x32x16(op[i], df[i], dp);
+#pragma unroll
+          for (int e = 0; e < EPM; ++e)  // P overwrites S in place
+            s[EPM * i + e] = fast_exp2(fmaf(s[EPM * i + e], c, -lse2));
+          __builtin_amdgcn_sched_barrier(0);
+        }
         uint32_t dsk[8];
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = fast_exp2(fmaf(s[i], c, -lse2));
-          const float p1 = fast_exp2(fmaf(s[i + 1], c, -lse2));
-          dsk[i >> 1] = pack_bf16x2(p0 * dp[i], p1 * dp[i + 1]);
-        }
+        for (int i = 0; i < 16; i += 2) dsk[i >> 1] = pack_bf16x2(s[i] * dp[i], s[i + 1] * dp[i + 1]);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const u32x4 bw = {dsk[4 * half], dsk[4 * half + 1], dsk[4 * half + 2],
