@@ -630,58 +630,66 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
     if (!packed || sees) {
       // straddles the rows' positions or their sample starts
       const bool straddle = !wave_live || klast > wqmin || kfirst < wqs_max;
+      static_assert(C::NKB == 2, "two 32-key blocks per tile");
+      constexpr int LA = 2;  // operand reads ahead of their contraction
+      constexpr int EPM = 16 / C::KS;  // vector items per contraction
+      f32x16 dinit;
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {  // 32 keys at a time
+      for (int i = 0; i < 16; ++i) dinit[i] = -delta;  // dP accumulates onto -delta
+      // S of block kb (K operands read LA contractions ahead), with side(i)
+      // after contraction i; a scheduling barrier after every group holds the
+      // order
+      auto scores = [&](int kb, auto side) {
         const int rb = kb * 32 * D * 2;
-        if (!packed && kb == 0) issue_tile(t + 1, Next{}, more);
-        f32x16 dinit;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dinit[i] = -delta;  // dP accumulates onto -delta
-        // S first, its K operands read two contractions ahead; then dP, its V
-        // operands likewise, with two of the exponentials of S after each of
-        // its contractions; a scheduling barrier after every group holds the
-        // order (otherwise the scheduler folds the reads back to read, wait,
-        // MFMA and the exponentials after the last contraction)
-        constexpr int LA = 2;
         bf16x8 op[C::KS];
 #pragma unroll
         for (int i = 0; i < LA; ++i) op[i] = lds_read_b128(kt, rb + koff[i]);
-        f32x16 s = f32x16{};
+        f32x16 sc = f32x16{};
 #pragma unroll
         for (int i = 0; i < C::KS; ++i) {
           if (i + LA < C::KS) op[i + LA] = lds_read_b128(kt, rb + koff[i + LA]);
-          s = mfma32x32x16(op[i], qf[i], s);
+          sc = mfma32x32x16(op[i], qf[i], sc);
+          side(i);
           __builtin_amdgcn_sched_barrier(0);
         }
+        return sc;
+      };
+      auto mask = [&](int kb, f32x16& sc) {
         if (straddle) {
           asm volatile("" ::: "memory");
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
             if constexpr (packed)  // qs <= k_pos <= qpos as one unsigned compare
-              s[i] = ((uint32_t)kp[key] - (uint32_t)qs > (uint32_t)qpos - (uint32_t)qs)
-                         ? -INFINITY : s[i];
+              sc[i] = ((uint32_t)kp[key] - (uint32_t)qs > (uint32_t)qpos - (uint32_t)qs)
+                          ? -INFINITY : sc[i];
             else
-              s[i] = (kp[key] > qpos) ? -INFINITY : s[i];
+              sc[i] = (kp[key] > qpos) ? -INFINITY : sc[i];
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+      };
+      // dP of block kb (V operands read LA ahead), the exponentials of its
+      // scores between its contractions (P overwrites S in place)
+      auto dprobs = [&](int kb, f32x16& sc) {
+        const int rb = kb * 32 * D * 2;
+        bf16x8 op[C::KS];
 #pragma unroll
         for (int i = 0; i < LA; ++i) op[i] = lds_read_b128(vt, rb + koff[i]);
         f32x16 dp = dinit;
-        constexpr int EPM = 16 / C::KS;  // exponentials per contraction
 #pragma unroll
         for (int i = 0; i < C::KS; ++i) {
           if (i + LA < C::KS) op[i + LA] = lds_read_b128(vt, rb + koff[i + LA]);
           dp = mfma32x32x16(op[i], df[i], dp);
 #pragma unroll
-          for (int e = 0; e < EPM; ++e)  // P overwrites S in place
-            s[EPM * i + e] = fast_exp2(fmaf(s[EPM * i + e], c, -lse2));
+          for (int e = 0; e < EPM; ++e)
+            sc[EPM * i + e] = fast_exp2(fmaf(sc[EPM * i + e], c, -lse2));
           __builtin_amdgcn_sched_barrier(0);
         }
-        uint32_t dsk[8];
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) dsk[i >> 1] = pack_bf16x2(s[i] * dp[i], s[i + 1] * dp[i + 1]);
+        return dp;
+      };
+      // dQ^T += K^T dS^T for block kb
+      auto dq_update = [&](int kb, const uint32_t (&dsk)[8]) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const u32x4 bw = {dsk[4 * half], dsk[4 * half + 1], dsk[4 * half + 2],
@@ -693,7 +701,27 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
             dqacc[mb] = mfma32x32x16(lds_read_tr(kt, rk + troff[0][mb], rk + troff[1][mb]), b,
                                      dqacc[mb]);
         }
-      }
+      };
+      // block 0: S, mask, dP with the exponentials; block 1's S then runs
+      // with block 0's dS between its contractions
+      if (!packed) issue_tile(t + 1, Next{}, more);
+      f32x16 s0 = scores(0, [](int) {});
+      mask(0, s0);
+      f32x16 dp0 = dprobs(0, s0);
+      uint32_t dsk0[8];
+      f32x16 s1 = scores(1, [&](int i) {
+#pragma unroll
+        for (int e = 0; e < EPM; e += 2)
+          dsk0[(EPM * i + e) >> 1] = pack_bf16x2(s0[EPM * i + e] * dp0[EPM * i + e],
+                                                 s0[EPM * i + e + 1] * dp0[EPM * i + e + 1]);
+      });
+      dq_update(0, dsk0);
+      mask(1, s1);
+      f32x16 dp1 = dprobs(1, s1);
+      uint32_t dsk1[8];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) dsk1[i >> 1] = pack_bf16x2(s1[i] * dp1[i], s1[i + 1] * dp1[i + 1]);
+      dq_update(1, dsk1);
     }
     if (more) {
       if (tid < C::BN) kpos_of(Next{})[tid] = key_live ? kpreg : kPosInf;
