@@ -263,13 +263,24 @@ int mmsp_attn_fwd_chunk_packed(const void* q, const void* k, const void* v,
  * Errors: NULL pointer (MMSP_ERR_NULL), sq or sk < 1 (MMSP_ERR_SHAPE),
  * plan_bytes too small (MMSP_ERR_WORKSPACE; also from the attention calls
  * given a non-NULL plan).  mmsp_attn_packed_plan_bytes returns 0 for sizes
- * below 1.  Cost: two small launches; tile lists longer than 32768 entries
- * are left in index order.
+ * below 1.  Cost: one small launch for sq, sk <= 8192 (two per chunk above);
+ * tile lists longer than 32768 entries are left in index order.
+ *
+ * mmsp_attn_packed_plans: the plans of n_chunks chunks in one launch, for
+ * chunks whose key positions lie back to back in k_pos (chunk c at
+ * k_pos + c * sk, as the slices of one balance permutation do); plan c is
+ * written at byte offset c * mmsp_attn_packed_plan_bytes(sq, sk) of `plans`,
+ * plans_bytes >= n_chunks times that (else MMSP_ERR_WORKSPACE).
+ * 1 <= n_chunks <= 1024 and n_chunks * sk < 2^31 (else MMSP_ERR_SHAPE).
+ * mmsp_attn_packed_plan is the case n_chunks = 1.
  */
 size_t mmsp_attn_packed_plan_bytes(int32_t sq, int32_t sk);
 int mmsp_attn_packed_plan(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
                           int32_t sq, int32_t sk, void* plan, size_t plan_bytes,
                           hipStream_t stream);
+int mmsp_attn_packed_plans(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
+                           int32_t n_chunks, int32_t sq, int32_t sk, void* plans,
+                           size_t plans_bytes, hipStream_t stream);
 
 /* ---- a3: log-sum-exp merge of two chunk results ---------------------------
  * The page's ring loop ("Implementation ...") adds each step's output into an

@@ -294,11 +294,18 @@ size_t mmsp_attn_packed_plan_bytes(int32_t sq, int32_t sk) {
 int mmsp_attn_packed_plan(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
                           int32_t sq, int32_t sk, void* plan, size_t plan_bytes,
                           hipStream_t stream) {
-  if (!q_pos || !q_start || !k_pos || !plan) return MMSP_ERR_NULL;
-  if (sq <= 0 || sk <= 0) return MMSP_ERR_SHAPE;
-  if (plan_bytes < mmsp::plan_shape(sq, sk).bytes()) return MMSP_ERR_WORKSPACE;
-  return check_hip(mmsp::launch_tile_plan(q_pos, q_start, k_pos, sq, sk,
-                                          static_cast<int32_t*>(plan), as_stream(stream)));
+  return mmsp_attn_packed_plans(q_pos, q_start, k_pos, 1, sq, sk, plan, plan_bytes, stream);
+}
+
+int mmsp_attn_packed_plans(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
+                           int32_t n_chunks, int32_t sq, int32_t sk, void* plans,
+                           size_t plans_bytes, hipStream_t stream) {
+  if (!q_pos || !q_start || !k_pos || !plans) return MMSP_ERR_NULL;
+  if (sq <= 0 || sk <= 0 || n_chunks <= 0 || n_chunks > kMaxRanks) return MMSP_ERR_SHAPE;
+  if ((long long)n_chunks * sk > kMaxElems) return MMSP_ERR_SHAPE;
+  if (plans_bytes / (size_t)n_chunks < mmsp::plan_shape(sq, sk).bytes()) return MMSP_ERR_WORKSPACE;
+  return check_hip(mmsp::launch_tile_plan(q_pos, q_start, k_pos, n_chunks, sq, sk,
+                                          static_cast<int32_t*>(plans), as_stream(stream)));
 }
 
 int mmsp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,

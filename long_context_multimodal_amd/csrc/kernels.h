@@ -66,8 +66,10 @@ struct PlanShape {
   size_t bytes() const { return 4 * (size_t)(kPlanHeader + 2 * (n_fwd + n_dq + n_dkdv)); }
 };
 PlanShape plan_shape(int sq, int sk);
+// plans of n_chunks chunks whose key positions lie sk apart in k_pos, written
+// to consecutive plans of PlanShape::bytes() each
 hipError_t launch_tile_plan(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
-                            int sq, int sk, int32_t* plan, hipStream_t stream);
+                            int n_chunks, int sq, int sk, int32_t* plan, hipStream_t stream);
 
 int fwd_rows_per_block();
 int fwd_keys_per_tile();

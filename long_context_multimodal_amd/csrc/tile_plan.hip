@@ -30,6 +30,7 @@ struct PlanArgs {
   int n_fwd, n_dq, n_dkdv;
   int fwd_off, dq_off, dkdv_off, work_off;
   int32_t* plan;
+  int plan_words;  // stride of consecutive plans (several chunks in one launch)
 };
 
 // Entries of the non-decreasing array a[0, n) below xa, and of b[0, n) at or
@@ -86,15 +87,19 @@ __device__ __forceinline__ void write_header(const PlanArgs& a) {
   a.plan[7] = 0;
 }
 
-// Shards of at most kSmallPlan positions (the usual case): one workgroup
-// stages the three position arrays in LDS, counts every tile's work there and
-// ranks the tiles, in one launch.
+// Shards of at most kSmallPlan positions (the usual case): one workgroup per
+// chunk stages the three position arrays in LDS, counts every tile's work
+// there and ranks the tiles; the chunks of one launch have consecutive key
+// positions (sk apart) and consecutive plans (plan_words apart).
 constexpr int kSmallPlan = 8192;
 constexpr int kSmallThreads = 1024;
 
-__global__ void __launch_bounds__(kSmallThreads) plan_small_kernel(PlanArgs a) {
+__global__ void __launch_bounds__(kSmallThreads) plan_small_kernel(PlanArgs args) {
   __shared__ int32_t s_q[kSmallPlan], s_s[kSmallPlan], s_k[kSmallPlan];
   __shared__ int32_t s_w[kSmallThreads];
+  PlanArgs a = args;
+  a.k_pos += (size_t)blockIdx.x * a.sk;
+  a.plan += (size_t)blockIdx.x * a.plan_words;
   const int tid = threadIdx.x;
   // every load issued before the first store: one memory round trip
   constexpr int PER = kSmallPlan / kSmallThreads;
@@ -185,7 +190,7 @@ PlanShape plan_shape(int sq, int sk) {
 }
 
 hipError_t launch_tile_plan(const int32_t* q_pos, const int32_t* q_start, const int32_t* k_pos,
-                            int sq, int sk, int32_t* plan, hipStream_t stream) {
+                            int n_chunks, int sq, int sk, int32_t* plan, hipStream_t stream) {
   const PlanShape s = plan_shape(sq, sk);
   PlanArgs a;
   a.q_pos = q_pos;
@@ -207,17 +212,25 @@ hipError_t launch_tile_plan(const int32_t* q_pos, const int32_t* q_start, const 
   a.dkdv_off = s.dkdv_off();
   a.work_off = s.work_off();
   a.plan = plan;
+  a.plan_words = (int)(s.bytes() / 4);
   const int total = s.n_fwd + s.n_dq + s.n_dkdv;
   if (sq <= kSmallPlan && sk <= kSmallPlan && total <= kSmallThreads) {
-    hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, a);
+    hipLaunchKernelGGL(plan_small_kernel, dim3(n_chunks), dim3(kSmallThreads), 0, stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(plan_work_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int nmax = max(s.n_fwd, max(s.n_dq, s.n_dkdv));
-  hipLaunchKernelGGL(plan_order_kernel, dim3((nmax + 255) / 256, 3), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  for (int c = 0; c < n_chunks; ++c) {
+    PlanArgs b = a;
+    b.k_pos = k_pos + (size_t)c * sk;
+    b.plan = plan + (size_t)c * a.plan_words;
+    hipLaunchKernelGGL(plan_work_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(plan_order_kernel, dim3((nmax + 255) / 256, 3), dim3(256), 0, stream, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mmsp

@@ -56,6 +56,7 @@ SIGNATURES = {
                                                   _U32, _VP, _VP, _VP, _VP]),
     "mmsp_attn_packed_plan_bytes": (_SZ, [_I32, _I32]),
     "mmsp_attn_packed_plan": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _VP, _SZ, _VP]),
+    "mmsp_attn_packed_plans": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _SZ, _VP]),
     "mmsp_ring_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
                                          _I32, _I32, _I32, _F32, _U32, _VP, _VP, _VP, _VP]),
     "mmsp_ring_backward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
@@ -293,6 +294,35 @@ def packed_plan(q_pos, q_start, k_pos, plan=None):
                                        _ptr(plan), plan.numel() * 4, _stream()),
            "mmsp_attn_packed_plan")
     return plan
+
+
+def packed_plans(q_pos, q_start, k_pos_all, n_chunks, plans=None):
+    """Tile plans of ``n_chunks`` chunks in one launch: ``k_pos_all`` (int32)
+    holds the chunks' key positions back to back, ``n_chunks * sk`` entries.
+    Returns an int32 tensor ``[n_chunks, words]`` whose row c is chunk c's
+    plan (as :func:`packed_plan` makes it); ``plans`` may be given to reuse a
+    buffer of that shape."""
+    import torch
+    _need(q_pos, torch.int32, "q_pos", 1)
+    _need(q_start, torch.int32, "q_start", 1)
+    _need(k_pos_all, torch.int32, "k_pos_all", 1)
+    sq = q_pos.numel()
+    if q_start.numel() != sq:
+        raise ValueError("q_start must have sq entries")
+    if n_chunks < 1 or k_pos_all.numel() % n_chunks:
+        raise ValueError("k_pos_all must hold n_chunks equal chunks")
+    sk = k_pos_all.numel() // n_chunks
+    nbytes = lib().mmsp_attn_packed_plan_bytes(sq, sk)
+    if nbytes == 0:
+        raise ValueError("positions must not be empty")
+    if plans is None:
+        plans = torch.empty((n_chunks, nbytes // 4), dtype=torch.int32, device=q_pos.device)
+    _need(plans, torch.int32, "plans", 2)
+    _shape(plans, (n_chunks, nbytes // 4), "plans")
+    _check(lib().mmsp_attn_packed_plans(_ptr(q_pos), _ptr(q_start), _ptr(k_pos_all), n_chunks,
+                                        sq, sk, _ptr(plans), plans.numel() * 4, _stream()),
+           "mmsp_attn_packed_plans")
+    return plans
 
 
 def attn_fwd_chunk(q, k, v, q_pos=None, k_pos=None, scale=None, causal=True, o=None, lse=None,

@@ -24,11 +24,35 @@ def ring_order(rank: int, n_chunks: int):
     return [(rank - t) % n_chunks for t in range(n_chunks)]
 
 
+def _back_to_back(k_pos_chunks):
+    """One view over all chunks' positions when they lie back to back in one
+    array (slices of one balance permutation), else None."""
+    import torch
+    first = k_pos_chunks[0]
+    n, sk = len(k_pos_chunks), first.numel()
+    for c, kp in enumerate(k_pos_chunks):
+        if (kp.dtype != torch.int32 or kp.device != first.device or kp.numel() != sk or
+                not kp.is_contiguous() or kp.data_ptr() != first.data_ptr() + 4 * c * sk):
+            return None
+    if first.untyped_storage().nbytes() < 4 * (first.storage_offset() + n * sk):
+        return None
+    return torch.as_strided(first, (n * sk,), (1,))
+
+
 def packed_plans(q_pos, q_start, k_pos_chunks, plans=None):
     """Tile plans of every chunk for packed samples (:func:`mmsp.packed_plan`),
-    indexed by chunk; one list serves the forward and the backward of a step.
-    ``plans`` may hold earlier plans whose buffers are reused."""
-    return [mmsp.packed_plan(q_pos, q_start, kp, plan=None if plans is None else plans[c])
+    indexed by chunk; one set serves the forward and the backward of a step.
+    When the chunks' positions lie back to back in one array, one launch makes
+    them all and the result is an int32 tensor whose row c is chunk c's plan;
+    otherwise a list.  ``plans`` (a result of this call) has its buffers
+    reused."""
+    import torch
+    k_all = _back_to_back(k_pos_chunks)
+    if k_all is not None:
+        block = plans if isinstance(plans, torch.Tensor) else None
+        return mmsp.packed_plans(q_pos, q_start, k_all, len(k_pos_chunks), plans=block)
+    reuse = plans if isinstance(plans, list) else None
+    return [mmsp.packed_plan(q_pos, q_start, kp, plan=None if reuse is None else reuse[c])
             for c, kp in enumerate(k_pos_chunks)]
 
 

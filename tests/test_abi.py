@@ -174,6 +174,13 @@ def test_packed_plan_size_and_rejects():
     assert f(FAKE, FAKE, FAKE, 0, 128, FAKE, need, None) == -2
     assert f(FAKE, FAKE, FAKE, 128, 0, FAKE, need, None) == -2
     assert f(FAKE, FAKE, FAKE, 128, 128, FAKE, need - 4, None) == -5
+    g = lib.mmsp_attn_packed_plans  # (q_pos, q_start, k_pos, n_chunks, sq, sk, plans, bytes)
+    assert g(None, FAKE, FAKE, 4, 128, 128, FAKE, 4 * need, None) == -1
+    assert g(FAKE, FAKE, FAKE, 4, 128, 128, None, 4 * need, None) == -1
+    assert g(FAKE, FAKE, FAKE, 0, 128, 128, FAKE, 4 * need, None) == -2
+    assert g(FAKE, FAKE, FAKE, 2000, 128, 128, FAKE, 2000 * need, None) == -2   # > 1024 chunks
+    assert g(FAKE, FAKE, FAKE, 1024, 128, 1 << 22, FAKE, 1 << 40, None) == -2  # n * sk >= 2^31
+    assert g(FAKE, FAKE, FAKE, 4, 128, 128, FAKE, 4 * need - 4, None) == -5    # one plan short
 
 
 def test_plan_rejected_without_packed_samples():

@@ -254,3 +254,33 @@ def test_packed_plan_leaves_results_unchanged(mm, lens, p, rank, hq, hkv, d):
     for name, got in outs.items():
         for x, y, what in zip(outs["none"], got, ("O", "LSE", "dQ", "dK", "dV")):
             assert torch.equal(x, y), f"{what} with plan '{name}'"
+
+
+@pytest.mark.parametrize("lens,p", [([1024, 512, 2048, 512], 2), ([32] * 20 + [640], 4),
+                                    ([8192, 4100, 12284, 8192], 2)])
+def test_batched_plans_equal_single_plans(mm, lens, p):
+    """The plans of all chunks in one launch (positions back to back) equal the
+    per-chunk plans bit for bit, also for shards above 8192 positions (the
+    two-kernel path); the ring helper takes the batched path for slices of one
+    permutation."""
+    mmsp, ring = mm
+    import torch
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    perm, first = oracle.zigzag_packed_perm(starts, p)
+    shard = perm.size // p
+    for rank in range(p):
+        qp = to_dev_i32(perm[rank * shard:(rank + 1) * shard])
+        qs = to_dev_i32(first[rank * shard:(rank + 1) * shard])
+        perm_d = to_dev_i32(perm)
+        kps = [perm_d[c * shard:(c + 1) * shard] for c in range(p)]
+        block = ring.packed_plans(qp, qs, kps)
+        assert isinstance(block, torch.Tensor) and block.shape[0] == p
+        for c in range(p):
+            single = mmsp.packed_plan(qp, qs, kps[c].contiguous().clone())
+            assert torch.equal(block[c], single), f"rank {rank} chunk {c}"
+        # reusing the buffers gives the same plans
+        again = ring.packed_plans(qp, qs, kps, plans=block.clone())
+        assert torch.equal(again, block)
+        # separate arrays take the per-chunk path
+        lst = ring.packed_plans(qp, qs, [k.clone() for k in kps])
+        assert isinstance(lst, list) and all(torch.equal(a, b) for a, b in zip(lst, block))
