@@ -348,6 +348,88 @@ def gemm_context(torch, iters, device, n=8192):
         return {"skipped": f"{type(e).__name__}: {str(e)[:200]}"}
 
 
+def fixed_cost_sweep(torch, mmsp, device, batch=8, reps=3):
+    """Fixed costs of the three attention kernels, per launch and per
+    workgroup.  Each kernel runs back to back on inputs where every query sees
+    every key (32 heads, d = 128, causal positions with all keys earlier), with
+    the inner tiles a workgroup walks and the workgroups per slot varied; a
+    least-squares fit of T = L + n * (tiles * t + F) gives L (per launch), t
+    (per inner tile and slot) and F (per workgroup).  A slot is one workgroup
+    place: one per CU for the forward, two for the backward kernels."""
+    h, d = 32, 128
+    cus = mmsp.device_info(0)["compute_units"]
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    big = [torch.randn((8192, h, d), generator=gen).to(torch.bfloat16).to(device)
+           for _ in range(4)]
+
+    def timed(call):
+        call()
+        ts = []
+        for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(batch):
+                call()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1000.0 / batch)
+        return sorted(ts)[len(ts) // 2]
+
+    def inputs(sq, sk):
+        qp = (1 << 20) + torch.arange(sq, dtype=torch.int32, device=device)
+        kp = torch.arange(sk, dtype=torch.int32, device=device)
+        return (big[0][:sq], big[1][:sk], big[2][:sk], big[3][:sq], qp, kp)
+
+    def fwd(sq, sk):
+        q, k, v, _, qp, kp = inputs(sq, sk)
+        o = torch.zeros((sq, h, d), dtype=torch.float32, device=device)
+        lse = torch.zeros((h, sq), dtype=torch.float32, device=device)
+        return timed(lambda: mmsp.attn_fwd_chunk(q, k, v, qp, kp, o=o, lse=lse, accumulate=True))
+
+    def bwd(part, sq, sk):
+        q, k, v, do, qp, kp = inputs(sq, sk)
+        lse = torch.full((h, sq), 12.0, dtype=torch.float32, device=device)
+        delta = torch.zeros((h, sq), dtype=torch.float32, device=device)
+        dq = torch.zeros((sq, h, d), dtype=torch.float32, device=device)
+        dk = torch.empty((sk, h, d), dtype=torch.float32, device=device)
+        dv = torch.empty((sk, h, d), dtype=torch.float32, device=device)
+        return timed(lambda: mmsp.attn_bwd_chunk(q, k, v, do, lse, delta, qp, kp, dq, dk, dv,
+                                                 part=part))
+
+    sizes = (1024, 2048, 4096, 8192)
+    runs = {
+        # kernel: (slots, [(sq, sk)], inner tiles a workgroup walks, workgroups, timed call)
+        "attn_fwd_kernel": (cus, [(sq, sk) for sq in (2048, 4096, 8192) for sk in sizes],
+                            lambda sq, sk: sk // 64, lambda sq, sk: sq // 256 * h,
+                            lambda sq, sk: fwd(sq, sk)),
+        "attn_bwd_dkdv_kernel": (2 * cus, [(sq, sk) for sk in (2048, 4096, 8192) for sq in sizes],
+                                 lambda sq, sk: sq // 32, lambda sq, sk: sk // 128 * h,
+                                 lambda sq, sk: bwd("dkdv", sq, sk)),
+        "attn_bwd_dq_kernel": (2 * cus, [(sq, sk) for sq in (2048, 4096, 8192) for sk in sizes],
+                               lambda sq, sk: sk // 64, lambda sq, sk: sq // 128 * h,
+                               lambda sq, sk: bwd("dq", sq, sk)),
+    }
+    out = {"what": "unmasked chunks, 32 heads, d = 128, launches back to back; "
+                   "T = L + n * (tiles * t + F), n = workgroups per slot", "kernels": {}}
+    for name, (slots, shapes, tiles_of, wgs_of, run) in runs.items():
+        rows, a, y = [], [], []
+        for sq, sk in shapes:
+            us = run(sq, sk)
+            n, tiles = wgs_of(sq, sk) / slots, tiles_of(sq, sk)
+            a.append([1.0, n * tiles, n])
+            y.append(us)
+            rows.append({"sq": sq, "sk": sk, "workgroups_per_slot": n, "tiles": tiles,
+                         "us": round(us, 1)})
+        sol = np.linalg.lstsq(np.array(a), np.array(y), rcond=None)[0]
+        for r, ai in zip(rows, a):
+            r["model_us"] = round(float(np.dot(sol, ai)), 1)
+        out["kernels"][name] = {"slots": slots, "L_us": round(float(sol[0]), 1),
+                                "t_us_per_tile": round(float(sol[1]), 3),
+                                "F_us_per_workgroup": round(float(sol[2]), 1),
+                                "F_in_tiles": round(float(sol[2] / sol[1]), 1), "runs": rows}
+    return out
+
+
 def device_record(torch, mmsp):
     """What the run was on: the peak the roofline uses is the published one
     (2.4 GHz); the clock the runtime reports and the one reached under load
@@ -404,6 +486,9 @@ def main():
                          "work-ordered tile plan made each step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--fixed-cost", action="store_true",
+                    help="time the attention kernels over workgroup lengths and counts and fit "
+                         "their fixed costs per launch and per workgroup (one JSON object)")
     args = ap.parse_args()
     if (args.graph or args.native_ring) and (args.ring_copy or args.rope_theta):
         print("--graph and --native-ring run the resident-chunk step without rotary passes; they "
@@ -434,6 +519,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+        return
+    if args.fixed_cost:
+        mmsp.lib()
+        print(json.dumps(fixed_cost_sweep(torch, mmsp, torch.device("cuda:0"))))
         return
     mmsp.lib()
     device = torch.device("cuda:0")
