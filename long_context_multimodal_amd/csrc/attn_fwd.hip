@@ -552,28 +552,42 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   }
 
   // ---- epilogue: normalise, then write or merge ----
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const float l_tot = sum_halves(l_run[qb]);
-    if (!row_ok[qb]) continue;
+  // A lane holds its row's head-dim entries in 16-byte pieces 32 bytes apart,
+  // so storing them directly writes every fp32 row of O in 32-byte pieces, and
+  // the workgroups of a plain causal launch end at about the same time, so
+  // those pieces reach the L2 together.  Each wave instead passes its 32 rows through LDS
+  // (the K/V ring is free after the loop) and reads and writes whole rows.
+  // The pieces go in 1 KiB blocks, one per (32-column block, 8-row group);
+  // lane L = 32 hh + r puts its piece in slot L ^ b ^ 8 hh of block b, so that
+  // every 16-lane group of a dump or of a read-back touches 16 bank groups.
+  static_assert(C::QB == 1, "one 32-row block per wave");
+  if (ACC && nt == 0) {  // merging with an empty result is the identity
+    wait_vmem_le<0>();
+    return;
+  }
+  if constexpr (PACKED) {
+    // Packed samples make many short workgroups that end at different times;
+    // there the LDS pass costs more than the whole-row stores save (~5% of
+    // the packed forward), so they store the 16-byte pieces directly.
+    const float l_tot = sum_halves(l_run[0]);
+    if (!row_ok[0]) return;
     const bool has = l_tot > 0.f;
     const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-    const float lse2 = has ? m_run[qb] + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    float* orow = p.o + ((size_t)row[qb] * p.hq + h) * D;
-    float* lrow = p.lse + (size_t)h * p.sq + row[qb];
+    const float lse2 = has ? m_run[0] + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    float* orow = p.o + ((size_t)row[0] * p.hq + h) * D;
+    float* lrow = p.lse + (size_t)h * p.sq + row[0];
     if (!ACC) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = mb * 32 + 8 * g + 4 * hh;
-          f32x4 val = {oacc[qb][mb][4 * g] * inv, oacc[qb][mb][4 * g + 1] * inv,
-                       oacc[qb][mb][4 * g + 2] * inv, oacc[qb][mb][4 * g + 3] * inv};
+          f32x4 val = {oacc[0][mb][4 * g] * inv, oacc[0][mb][4 * g + 1] * inv,
+                       oacc[0][mb][4 * g + 2] * inv, oacc[0][mb][4 * g + 3] * inv};
           *(f32x4*)(orow + d0) = val;
         }
       if (hh == 0) *lrow = has ? lse2 * kLn2 : -INFINITY;
-    } else {
-      if (!has) continue;  // merging with an empty result is the identity
+    } else if (has) {  // merging with an empty result is the identity
       const float la2 = *lrow * kLog2e;  // -inf stays -inf
       const float mx = fmaxf(la2, lse2);
       const float ea = fast_exp2(la2 - mx), eb = fast_exp2(lse2 - mx);
@@ -588,10 +602,88 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
           const f32x4 old = *(const f32x4*)(orow + d0);
           f32x4 val;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = fmaf(wa, old[e], wb * oacc[qb][mb][4 * g + e]);
+          for (int e = 0; e < 4; ++e) val[e] = fmaf(wa, old[e], wb * oacc[0][mb][4 * g + e]);
           *(f32x4*)(orow + d0) = val;
         }
       if (hh == 0) *lrow = (mx + __builtin_amdgcn_logf(tot)) * kLn2;
+    }
+    return;
+  }
+  wait_vmem_le<0>();  // no direct load into the ring still in flight
+  __syncthreads();    // and no wave still reading it
+  const float l_tot = sum_halves(l_run[0]);
+  const bool has = l_tot > 0.f;
+  const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+  const float lse2 = has ? m_run[0] + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+  // the lane's row: new O = wa * O_acc + wb * (unnormalised O of this chunk);
+  // wa < 0 leaves the row as it is
+  float wa = 0.f, wb = inv;
+  if (row_ok[0]) {
+    float* lrow = p.lse + (size_t)h * p.sq + row[0];
+    if (!ACC) {
+      if (hh == 0) *lrow = has ? lse2 * kLn2 : -INFINITY;
+    } else if (!has) {
+      wa = -1.f;  // merging with an empty result is the identity
+    } else {
+      const float la2 = *lrow * kLog2e;  // -inf stays -inf
+      const float mx = fmaxf(la2, lse2);
+      const float ea = fast_exp2(la2 - mx), eb = fast_exp2(lse2 - mx);
+      const float tot = ea + eb;
+      const float rt = __builtin_amdgcn_rcpf(tot);
+      wa = ea * rt;
+      wb = eb * rt * inv;
+      if (hh == 0) *lrow = (mx + __builtin_amdgcn_logf(tot)) * kLn2;
+    }
+  }
+  // waves 2s and 2s + 1 use stage s: one tile each for their 32 rows of fp32 O
+  // (32 x D x 4 bytes = one K or V tile), their row factors in its position slots
+  static_assert(32 * D * 4 == C::TILE && 2 * 32 * 4 <= C::WAVES * C::BN * 4,
+                "two waves' rows and row factors fit one stage");
+  const int w2 = wave >> 1;
+  lds_char* stg = w2 == 0 ? (lds_char*)sS0 : w2 == 1 ? (lds_char*)sS1
+                : w2 == 2 ? (lds_char*)sS2 : (lds_char*)sS3;
+  lds_char* reg = stg + (wave & 1) * C::TILE;
+  float* wa_s = (float*)(stg + 2 * C::TILE) + (wave & 1) * 32;
+  if (ACC && hh == 0) wa_s[l32] = wa;
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int b = mb * 4 + g;
+      const f32x4 v4 = {oacc[0][mb][4 * g] * wb, oacc[0][mb][4 * g + 1] * wb,
+                        oacc[0][mb][4 * g + 2] * wb, oacc[0][mb][4 * g + 3] * wb};
+      *(__attribute__((address_space(3))) f32x4*)(reg + b * 1024 + ((lane ^ b ^ (hh << 3)) << 4)) =
+          v4;
+    }
+  wait_lds_writes();
+  // read back: step i covers rows rr = (64 i + lane) / CH, piece cc = lane % CH
+  // (columns 4 cc .. 4 cc + 3), which sits in block cc / 2, lane slot
+  // (cc % 2) * 32 + rr
+  constexpr int CH = D / 4;
+  constexpr int READS = 32 * CH / kWave;
+  const int cc = lane % CH;
+  const int rb = cc >> 1;
+  const lds_char* rbase = reg + rb * 1024;
+#pragma unroll
+  for (int i = 0; i < READS; ++i) {
+    const int rr = (i * kWave + lane) / CH;
+    const int slot = ((cc & 1) << 5) | rr;
+    f32x4 v4 = *(const __attribute__((address_space(3))) f32x4*)(
+        rbase + ((slot ^ rb ^ ((cc & 1) << 3)) << 4));
+    const int r = wr0 + rr;
+    if (r < p.sq) {
+      float* dst = p.o + ((size_t)r * p.hq + h) * D + cc * 4;
+      if (ACC) {
+        const float a = wa_s[rr];
+        if (a >= 0.f) {
+          const f32x4 old = *(const f32x4*)dst;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = fmaf(a, old[e], v4[e]);
+          *(f32x4*)dst = v4;
+        }
+      } else {
+        *(f32x4*)dst = v4;
+      }
     }
   }
 }
