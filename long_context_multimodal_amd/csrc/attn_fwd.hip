@@ -609,8 +609,24 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     }
     return;
   }
-  wait_vmem_le<0>();  // no direct load into the ring still in flight
-  __syncthreads();    // and no wave still reading it
+  // The reads of the running result go out first, before the barrier: the
+  // lane's row of LSE_acc, then every O_acc piece this lane merges below
+  // (rows past sq read the last row and are not stored).
+  constexpr int CH = D / 4;               // 16-byte pieces per fp32 row
+  constexpr int READS = 32 * CH / kWave;  // pieces per lane
+  const int cc = lane % CH;
+  float la_raw = 0.f;
+  f32x4 old[READS];
+  if constexpr (ACC) {
+    la_raw = p.lse[(size_t)h * p.sq + min(row[0], p.sq - 1)];
+#pragma unroll
+    for (int i = 0; i < READS; ++i) {
+      const int r = min(wr0 + (i * kWave + lane) / CH, p.sq - 1);
+      old[i] = *(const f32x4*)(p.o + ((size_t)r * p.hq + h) * D + cc * 4);
+    }
+  }
+  wait_vmem_le<ACC ? READS + 1 : 0>();  // the direct loads into the ring have landed
+  barrier_only();                       // and no wave reads the ring any more
   const float l_tot = sum_halves(l_run[0]);
   const bool has = l_tot > 0.f;
   const float inv = has ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
@@ -625,7 +641,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
     } else if (!has) {
       wa = -1.f;  // merging with an empty result is the identity
     } else {
-      const float la2 = *lrow * kLog2e;  // -inf stays -inf
+      const float la2 = la_raw * kLog2e;  // -inf stays -inf
       const float mx = fmaxf(la2, lse2);
       const float ea = fast_exp2(la2 - mx), eb = fast_exp2(lse2 - mx);
       const float tot = ea + eb;
@@ -659,32 +675,30 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   // read back: step i covers rows rr = (64 i + lane) / CH, piece cc = lane % CH
   // (columns 4 cc .. 4 cc + 3), which sits in block cc / 2, lane slot
   // (cc % 2) * 32 + rr
-  constexpr int CH = D / 4;
-  constexpr int READS = 32 * CH / kWave;
-  const int cc = lane % CH;
+  // (all pieces are read before the first store, so the reads overlap)
   const int rb = cc >> 1;
   const lds_char* rbase = reg + rb * 1024;
+  f32x4 piece[READS];
+  float a[READS];
 #pragma unroll
   for (int i = 0; i < READS; ++i) {
     const int rr = (i * kWave + lane) / CH;
     const int slot = ((cc & 1) << 5) | rr;
-    f32x4 v4 = *(const __attribute__((address_space(3))) f32x4*)(
+    piece[i] = *(const __attribute__((address_space(3))) f32x4*)(
         rbase + ((slot ^ rb ^ ((cc & 1) << 3)) << 4));
-    const int r = wr0 + rr;
-    if (r < p.sq) {
-      float* dst = p.o + ((size_t)r * p.hq + h) * D + cc * 4;
-      if (ACC) {
-        const float a = wa_s[rr];
-        if (a >= 0.f) {
-          const f32x4 old = *(const f32x4*)dst;
+    a[i] = ACC ? wa_s[rr] : 0.f;
+  }
+  wait_lds_writes();  // lgkmcnt(0): every read above has returned
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = fmaf(a, old[e], v4[e]);
-          *(f32x4*)dst = v4;
-        }
-      } else {
-        *(f32x4*)dst = v4;
-      }
+  for (int i = 0; i < READS; ++i) {
+    const int r = wr0 + (i * kWave + lane) / CH;
+    f32x4 v4 = piece[i];
+    if constexpr (ACC) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = fmaf(a[i], old[i][e], v4[e]);
     }
+    if (r < p.sq && (!ACC || a[i] >= 0.f))
+      *(f32x4*)(p.o + ((size_t)r * p.hq + h) * D + cc * 4) = v4;
   }
 }
 
