@@ -110,15 +110,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   wkmin = uniform(wkmin);
   wkmax = uniform(wkmax);
   int qstart = 0;
-  if (p.causal && !PACKED) {
-    const int kmin = p.k_pos[j0];
-    int lo = 0, hi = p.sq;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (p.q_pos[mid] < kmin) lo = mid + 1; else hi = mid;
-    }
-    qstart = lo;
-  }
+  if (p.causal && !PACKED) qstart = wave_prefix<false>(p.q_pos, p.sq, p.k_pos[j0]);
   // packed samples: only queries whose sample starts at or before the
   // workgroup's last key can see it (sample starts are non-decreasing); both
   // ends come from one wave-wide search (the plain instance keeps the binary
@@ -442,18 +434,31 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
         *(__attribute__((address_space(3))) f32x4*)(blk + ((lane ^ b ^ (hh << 3)) << 4)) = v4;
       }
     wait_lds_writes();
+    // the pieces are read (and, to accumulate, the old values loaded) eight
+    // at a time before any of them is stored, so the reads overlap
+    constexpr int GRP = READS < 8 ? READS : 8;
 #pragma unroll
-    for (int i = 0; i < READS; ++i) {
-      const int rr = (i * kWave + lane) / CH;
-      const int slot = ((cc & 1) << 5) | rr;
-      const f32x4 v4 = *(const __attribute__((address_space(3))) f32x4*)(
-          rbase + ((slot ^ rb ^ ((cc & 1) << 3)) << 4));
-      const int k = wk0 + rr;
-      if (k < p.sk) {
-        float* dst = out + (size_t)k * kv_stride + (size_t)kvh * D + cc * 4;
-        f32x4 w = v4;
-        if (p.accumulate) w += *(const f32x4*)dst;
-        *(f32x4*)dst = w;
+    for (int i0 = 0; i0 < READS; i0 += GRP) {
+      f32x4 piece[GRP];
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const int rr = ((i0 + j) * kWave + lane) / CH;
+        const int slot = ((cc & 1) << 5) | rr;
+        piece[j] = *(const __attribute__((address_space(3))) f32x4*)(
+            rbase + ((slot ^ rb ^ ((cc & 1) << 3)) << 4));
+      }
+      wait_lds_writes();  // lgkmcnt(0): every read above has returned
+      if (p.accumulate) {
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) {  // keys past sk read the last key and are not stored
+          const int k = min(wk0 + ((i0 + j) * kWave + lane) / CH, p.sk - 1);
+          piece[j] += *(const f32x4*)(out + (size_t)k * kv_stride + (size_t)kvh * D + cc * 4);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const int k = wk0 + ((i0 + j) * kWave + lane) / CH;
+        if (k < p.sk) *(f32x4*)(out + (size_t)k * kv_stride + (size_t)kvh * D + cc * 4) = piece[j];
       }
     }
   };
