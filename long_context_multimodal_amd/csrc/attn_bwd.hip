@@ -27,7 +27,7 @@
 // the L2 and cost more than the recomputation.
 //
 // Causal skipping in both: the key (or query) range of a workgroup is
-// bounded by a binary search on the sorted positions, waves skip tiles they
+// bounded by a wave-wide search on the sorted positions, waves skip tiles they
 // cannot see and mask only the tiles that straddle their positions.  Packed
 // samples (a per-query sample start bounding the keys from below) run in
 // their own template instances.  Either kernel can be enqueued alone
@@ -98,28 +98,34 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   const bool key_ok = key < p.sk;
   const size_t kv_stride = (size_t)p.hkv * D;
 
-  const int kpos = key_ok ? (p.causal ? p.k_pos[key] : 0) : kPosInf;
+  // Every key position the prologue needs is read in one group (indices
+  // clamped into the chunk), so the reads overlap instead of waiting on one
+  // another; then one wave-wide search finds the visible query range.
+  const int sk1 = p.sk - 1;
   const int wk0 = j0 + wave * 32;
   const bool wave_live = wk0 < p.sk;
   const bool wave_full_keys = wk0 + 31 < p.sk;
-  int wkmin = kPosInf, wkmax = kPosInf;
-  if (wave_live) {
-    wkmin = p.causal ? p.k_pos[wk0] : 0;
-    wkmax = p.causal ? p.k_pos[min(wk0 + 31, p.sk - 1)] : 0;
+  int v_key = 0, v_w0 = 0, v_wend = 0, v_j0 = 0, v_jend = 0;
+  if (p.causal) {
+    v_key = p.k_pos[min(key, sk1)];
+    v_w0 = p.k_pos[min(wk0, sk1)];
+    v_wend = p.k_pos[min(wk0 + 31, sk1)];
+    v_j0 = p.k_pos[j0];
+    v_jend = p.k_pos[min(j0 + C::BK - 1, sk1)];
   }
-  wkmin = uniform(wkmin);
-  wkmax = uniform(wkmax);
-  int qstart = 0;
-  if (p.causal && !PACKED) qstart = wave_prefix<false>(p.q_pos, p.sq, p.k_pos[j0]);
-  // packed samples: only queries whose sample starts at or before the
-  // workgroup's last key can see it (sample starts are non-decreasing); both
-  // ends come from one wave-wide search (the plain instance keeps the binary
-  // search above: the wave-wide one pushes its registers past 256)
+  const int kpos = key_ok ? v_key : kPosInf;
+  const int wkmin = uniform(wave_live ? v_w0 : kPosInf);
+  const int wkmax = uniform(wave_live ? v_wend : kPosInf);
+  // queries at or after the workgroup's first key position and, with packed
+  // samples, whose sample starts at or before its last key (sample starts
+  // are non-decreasing): both ends from one wave-wide search
   constexpr bool packed = PACKED;  // q_start given
-  int qend = p.sq;
-  if (packed) {
-    const int kmin = p.k_pos[j0], kmax = p.k_pos[min(j0 + C::BK - 1, p.sk - 1)];
-    wave_prefix_two<false, true>(p.q_pos, p.sq, kmin, p.q_start, p.sq, kmax, qstart, qend);
+  int qstart = 0, qend = p.sq;
+  if (p.causal) {
+    if constexpr (packed)
+      wave_prefix_two<false, true>(p.q_pos, p.sq, v_j0, p.q_start, p.sq, v_jend, qstart, qend);
+    else
+      qstart = wave_prefix<false>(p.q_pos, p.sq, v_j0);
   }
   const int n_qt = uniform((qend + C::BQ - 1) / C::BQ);
   const int qt0 = qstart / C::BQ;
@@ -514,39 +520,46 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdParams p) {
   const int row = q0 + wave * 32 + l32;
   const bool row_ok = row < p.sq;
 
-  int qpos = INT_MIN;
-  float lse2 = INFINITY, delta = 0.f;
-  if (row_ok) {
-    qpos = p.causal ? p.q_pos[row] : (kPosInf - 1);
-    const float l = p.lse[(size_t)h * p.sq + row];
-    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
-    delta = p.delta[(size_t)h * p.sq + row];
-  }
+  // Every position, sample start and row statistic the prologue needs is
+  // read in one group (indices clamped into the shard, results discarded
+  // where out of range), so the reads overlap instead of waiting on one another.
+  constexpr bool packed = PACKED;  // q_start given (keys below a row's sample start are hidden)
+  const int sq1 = p.sq - 1;
   const int wr0 = q0 + wave * 32;
   const bool wave_live = wr0 < p.sq;
-  int wqmin = 0, wqmax = INT_MIN;
-  if (wave_live) {
-    const int wlast = min(wr0 + 31, p.sq - 1);
-    wqmin = p.causal ? p.q_pos[wr0] : (kPosInf - 1);
-    wqmax = p.causal ? p.q_pos[wlast] : (kPosInf - 1);
+  const int rc = min(row, sq1);
+  const float l_raw = p.lse[(size_t)h * p.sq + rc];
+  const float d_raw = p.delta[(size_t)h * p.sq + rc];
+  int v_row = kPosInf - 1, v_w0 = kPosInf - 1, v_wend = kPosInf - 1, v_qend = kPosInf - 1;
+  if (p.causal) {
+    v_row = p.q_pos[rc];
+    v_w0 = p.q_pos[min(wr0, sq1)];
+    v_wend = p.q_pos[min(wr0 + 31, sq1)];
+    v_qend = p.q_pos[min(q0 + C::BM - 1, sq1)];
   }
-  wqmin = uniform(wqmin);
-  wqmax = uniform(wqmax);
-  // packed samples: keys below a row's sample start are hidden too
-  constexpr bool packed = PACKED;  // q_start given
-  const int qs = (packed && row_ok) ? p.q_start[row] : INT_MIN;
-  const int wqs_min = uniform((packed && wave_live) ? p.q_start[wr0] : INT_MIN);
-  const int wqs_max =
-      uniform((packed && wave_live) ? p.q_start[min(wr0 + 31, p.sq - 1)] : INT_MIN);
+  int v_qs = INT_MIN, v_wqs0 = INT_MIN, v_wqs1 = INT_MIN, v_q0s = INT_MIN;
+  if constexpr (packed) {
+    v_qs = p.q_start[rc];
+    v_wqs0 = p.q_start[min(wr0, sq1)];
+    v_wqs1 = p.q_start[min(wr0 + 31, sq1)];
+    v_q0s = p.q_start[min(q0, sq1)];
+  }
+  const int qpos = row_ok ? v_row : INT_MIN;
+  const float lse2 = !row_ok ? INFINITY : (l_raw == -INFINITY) ? INFINITY : l_raw * kLog2e;
+  const float delta = row_ok ? d_raw : 0.f;
+  const int wqmin = uniform(wave_live ? v_w0 : 0);
+  const int wqmax = uniform(wave_live ? v_wend : INT_MIN);
+  const int qs = row_ok ? v_qs : INT_MIN;
+  const int wqs_min = uniform(wave_live ? v_wqs0 : INT_MIN);
+  const int wqs_max = uniform(wave_live ? v_wqs1 : INT_MIN);
   // key range of the workgroup: [kbeg, nk) -- keys at or below its last
   // position and, with packed samples, at or after its first sample start
   int nk = p.sk, kbeg = 0;
   if (p.causal) {
-    const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
     if constexpr (packed)
-      wave_prefix_two<true, false>(p.k_pos, p.sk, qmax, p.k_pos, p.sk, p.q_start[q0], nk, kbeg);
+      wave_prefix_two<true, false>(p.k_pos, p.sk, v_qend, p.k_pos, p.sk, v_q0s, nk, kbeg);
     else
-      nk = wave_prefix<true>(p.k_pos, p.sk, qmax);
+      nk = wave_prefix<true>(p.k_pos, p.sk, v_qend);
   }
   const int tb = uniform(kbeg / C::BN);  // first tile
   const int nt = uniform(max(0, (nk + C::BN - 1) / C::BN - tb));

@@ -40,7 +40,7 @@
 //    tile back through the max-and-rescale path (the scores are still in
 //    registers; the packed path recomputes them from the K tile in LDS);
 //    row sums stay in fp32 (exact LSE for the merge and the backward);
-//  * causal tile skipping from the sorted positions: a binary search bounds
+//  * causal tile skipping from the sorted positions: a wave-wide search bounds
 //    the key range of the workgroup, each wave skips tiles it cannot see and
 //    masks only the tiles that straddle its rows' positions (or the tail),
 //    with one unsigned compare per score (sample start <= key position <=
@@ -120,41 +120,59 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_kernel(FwdParams p) {
   const int wr0 = q0 + wave * 32 * C::QB;  // first row of this wave
 
   // ---- positions: per lane and block, per block range, workgroup range ----
-  int row[C::QB], qpos[C::QB], bmin[C::QB];
+  // Every position and sample start the prologue needs is read in one group
+  // (indices clamped into the shard, results discarded where out of range),
+  // so the reads overlap instead of waiting on one another.
+  constexpr bool packed = PACKED;  // q_start given (keys below a row's sample start are hidden)
+  const int sq1 = p.sq - 1;
+  int row[C::QB], qpos[C::QB], bmin[C::QB], qs[C::QB], bqs_max[C::QB];
   bool row_ok[C::QB];
+  int v_row[C::QB], v_r0[C::QB], v_qs[C::QB], v_bqs[C::QB];
+  int v_wend = kPosInf - 1, v_qend = kPosInf - 1, v_wqs = INT_MIN, v_q0s = INT_MIN;
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     row[qb] = wr0 + 32 * qb + l32;
     row_ok[qb] = row[qb] < p.sq;
-    qpos[qb] = INT_MIN;
-    if (row_ok[qb]) qpos[qb] = p.causal ? p.q_pos[row[qb]] : (kPosInf - 1);
-    const int r0 = wr0 + 32 * qb;
-    bmin[qb] = uniform(r0 < p.sq ? (p.causal ? p.q_pos[r0] : (kPosInf - 1)) : kPosInf);
+    v_row[qb] = v_r0[qb] = kPosInf - 1;
+    v_qs[qb] = v_bqs[qb] = INT_MIN;
   }
-  const bool wave_live = wr0 < p.sq;
-  const int wqmax =
-      uniform(wave_live ? (p.causal ? p.q_pos[min(wr0 + 32 * C::QB - 1, p.sq - 1)] : kPosInf - 1)
-                        : INT_MIN);
-  // packed samples: keys below a row's sample start are hidden too
-  // (q_start is non-decreasing along the rows, like the positions)
-  constexpr bool packed = PACKED;  // q_start given
-  int qs[C::QB], bqs_max[C::QB];
+  if (p.causal) {
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      v_row[qb] = p.q_pos[min(row[qb], sq1)];
+      v_r0[qb] = p.q_pos[min(wr0 + 32 * qb, sq1)];
+    }
+    v_wend = p.q_pos[min(wr0 + 32 * C::QB - 1, sq1)];
+    v_qend = p.q_pos[min(q0 + C::BM - 1, sq1)];
+  }
+  if constexpr (packed) {
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      v_qs[qb] = p.q_start[min(row[qb], sq1)];
+      v_bqs[qb] = p.q_start[min(wr0 + 32 * qb + 31, sq1)];
+    }
+    v_wqs = p.q_start[min(wr0, sq1)];
+    v_q0s = p.q_start[min(q0, sq1)];
+  }
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
-    qs[qb] = (packed && row_ok[qb]) ? p.q_start[row[qb]] : INT_MIN;
     const int r0 = wr0 + 32 * qb;
-    bqs_max[qb] = uniform((packed && r0 < p.sq) ? p.q_start[min(r0 + 31, p.sq - 1)] : INT_MIN);
+    qpos[qb] = row_ok[qb] ? v_row[qb] : INT_MIN;
+    bmin[qb] = uniform(r0 < p.sq ? v_r0[qb] : kPosInf);
+    qs[qb] = row_ok[qb] ? v_qs[qb] : INT_MIN;
+    bqs_max[qb] = uniform(r0 < p.sq ? v_bqs[qb] : INT_MIN);
   }
-  const int wqs_min = uniform((packed && wave_live) ? p.q_start[wr0] : INT_MIN);
+  const bool wave_live = wr0 < p.sq;
+  const int wqmax = uniform(wave_live ? v_wend : INT_MIN);
+  const int wqs_min = uniform(wave_live ? v_wqs : INT_MIN);
   // key range of the workgroup: [kbeg, nk) -- keys at or below its last
   // position and, with packed samples, at or after its first sample start
   int nk = p.sk, kbeg = 0;
   if (p.causal) {
-    const int qmax = p.q_pos[min(q0 + C::BM - 1, p.sq - 1)];
     if constexpr (packed)
-      wave_prefix_two<true, false>(p.k_pos, p.sk, qmax, p.k_pos, p.sk, p.q_start[q0], nk, kbeg);
+      wave_prefix_two<true, false>(p.k_pos, p.sk, v_qend, p.k_pos, p.sk, v_q0s, nk, kbeg);
     else
-      nk = wave_prefix<true>(p.k_pos, p.sk, qmax);
+      nk = wave_prefix<true>(p.k_pos, p.sk, v_qend);
   }
   const int tb = uniform(kbeg / C::BN);  // first tile
   const int nt = uniform(max(0, (nk + C::BN - 1) / C::BN - tb));
