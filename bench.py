@@ -348,6 +348,16 @@ def gemm_context(torch, iters, device, n=8192):
         return {"skipped": f"{type(e).__name__}: {str(e)[:200]}"}
 
 
+def fit_fixed_costs(points):
+    """Least-squares fit of T = L + n * (tiles * t + F) to ``(n, tiles, T)``
+    points (n workgroups per slot, each walking ``tiles`` inner tiles):
+    returns ``(L, t, F)``, the cost per launch, per inner tile and slot, and
+    per workgroup."""
+    a = np.array([[1.0, n * tiles, n] for n, tiles, _ in points])
+    y = np.array([float(t) for *_, t in points])
+    return tuple(float(x) for x in np.linalg.lstsq(a, y, rcond=None)[0])
+
+
 def fixed_cost_sweep(torch, mmsp, device, batch=8, reps=3):
     """Fixed costs of the three attention kernels, per launch and per
     workgroup.  Each kernel runs back to back on inputs where every query sees
@@ -412,17 +422,16 @@ def fixed_cost_sweep(torch, mmsp, device, batch=8, reps=3):
     out = {"what": "unmasked chunks, 32 heads, d = 128, launches back to back; "
                    "T = L + n * (tiles * t + F), n = workgroups per slot", "kernels": {}}
     for name, (slots, shapes, tiles_of, wgs_of, run) in runs.items():
-        rows, a, y = [], [], []
+        rows, points = [], []
         for sq, sk in shapes:
             us = run(sq, sk)
             n, tiles = wgs_of(sq, sk) / slots, tiles_of(sq, sk)
-            a.append([1.0, n * tiles, n])
-            y.append(us)
+            points.append((n, tiles, us))
             rows.append({"sq": sq, "sk": sk, "workgroups_per_slot": n, "tiles": tiles,
                          "us": round(us, 1)})
-        sol = np.linalg.lstsq(np.array(a), np.array(y), rcond=None)[0]
-        for r, ai in zip(rows, a):
-            r["model_us"] = round(float(np.dot(sol, ai)), 1)
+        sol = fit_fixed_costs(points)
+        for r, (n, tiles, _) in zip(rows, points):
+            r["model_us"] = round(sol[0] + n * (tiles * sol[1] + sol[2]), 1)
         out["kernels"][name] = {"slots": slots, "L_us": round(float(sol[0]), 1),
                                 "t_us_per_tile": round(float(sol[1]), 3),
                                 "F_us_per_workgroup": round(float(sol[2]), 1),

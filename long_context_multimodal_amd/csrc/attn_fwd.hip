@@ -55,7 +55,11 @@
 //    query heads of one KV head on one XCD (shared L2) and dispatches the
 //    heavier (causally longer) query tiles first; when one head's tiles span
 //    several XCDs, heavy and light tiles alternate in blocks of 8 so every
-//    XCD and shader engine gets an even share.
+//    XCD and shader engine gets an even share;
+//  * epilogue (plain instances): each wave passes its 32 rows of fp32 O
+//    through the free K/V ring and reads O_acc and writes O in whole rows,
+//    with the running result's reads issued before the loop's closing
+//    barrier; packed instances store their 16-byte pieces directly.
 #include <type_traits>
 
 #include "common.h"
