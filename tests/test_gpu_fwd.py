@@ -80,6 +80,37 @@ def test_chunk_fully_masked_rows_and_tiles(mm):
     assert_close_abs(lse, l_ref, what="LSE")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_merge_with_rows_that_see_nothing(mm, d):
+    """The fused merge (MMSP_ACCUMULATE) on a chunk that some rows of one
+    workgroup see and others do not: rows 0..199 see none of chunk B, so
+    merging B leaves their O and LSE exactly as chunk A left them, while rows
+    200..399 of the same workgroups (and waves) merge; the second workgroup
+    ends in a ragged tail.  The result equals attention over both chunks' keys."""
+    import torch
+    mmsp, _ = mm
+    sq, sk, h = 400, 256, 4
+    qp = np.concatenate([600 + np.arange(200), 1000 + 3 * np.arange(200)]).astype(np.int32)
+    kp_a = (2 * np.arange(sk)).astype(np.int32)
+    kp_b = (1000 + 2 * np.arange(sk)).astype(np.int32)
+    qb, qv, kb, kv, vb, vv = _tensors(31 + d, sq, sk, h, h, d, n_chunks=2)
+    q = to_dev_bf16(qb)
+    o, lse = mmsp.attn_fwd_chunk(q, to_dev_bf16(kb[0]), to_dev_bf16(vb[0]), to_dev_i32(qp),
+                                 to_dev_i32(kp_a))
+    o_a, lse_a = to_np(o).copy(), to_np(lse).copy()
+    mmsp.attn_fwd_chunk(q, to_dev_bf16(kb[1]), to_dev_bf16(vb[1]), to_dev_i32(qp),
+                        to_dev_i32(kp_b), o=o, lse=lse, accumulate=True)
+    torch.cuda.synchronize()
+    o_m, lse_m = to_np(o), to_np(lse)
+    assert np.array_equal(o_m[:200], o_a[:200]) and np.array_equal(lse_m[:, :200], lse_a[:, :200])
+    assert not np.array_equal(o_m[200:], o_a[200:])
+    o_ref, l_ref = oracle.attention_forward(qv, np.concatenate([kv[0], kv[1]]),
+                                            np.concatenate([vv[0], vv[1]]), qp,
+                                            np.concatenate([kp_a, kp_b]))
+    assert_close_abs(o_m, o_ref, what="O")
+    assert_close_abs(lse_m, l_ref, what="LSE")
+
+
 def test_chunk_peaked_softmax(mm):
     # Q x 4 makes the softmax peaked and stresses the running-max rescale
     sq = sk = 512
