@@ -381,30 +381,6 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdParams p) {
   // L = 32 hh + r's piece in slot L ^ b ^ 8 hh: each dump is a 1 KiB write
   // whose 16-lane groups cover 16 bank groups, and so are the 16-lane groups
   // that read back one row's pieces (blocks b = 0..7 of both halves hh).
-  if constexpr (PACKED) {
-    // Packed samples make many short workgroups, which the LDS pass below
-    // costs ~2% of their time; they store the 16-byte pieces directly.
-    if (!key_ok) return;
-    float* dkr = p.dk + (size_t)key * kv_stride + (size_t)kvh * D;
-    float* dvr = p.dv + (size_t)key * kv_stride + (size_t)kvh * D;
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = mb * 32 + 8 * g + 4 * hh;
-        f32x4 kv4 = {dkacc[mb][4 * g] * p.scale, dkacc[mb][4 * g + 1] * p.scale,
-                     dkacc[mb][4 * g + 2] * p.scale, dkacc[mb][4 * g + 3] * p.scale};
-        f32x4 vv4 = {dvacc[mb][4 * g], dvacc[mb][4 * g + 1], dvacc[mb][4 * g + 2],
-                     dvacc[mb][4 * g + 3]};
-        if (p.accumulate) {
-          kv4 += *(const f32x4*)(dkr + d0);
-          vv4 += *(const f32x4*)(dvr + d0);
-        }
-        *(f32x4*)(dkr + d0) = kv4;
-        *(f32x4*)(dvr + d0) = vv4;
-      }
-    return;
-  }
   if (!wave_live) return;
   constexpr int NB = C::MB * 4;          // 1 KiB blocks per accumulator
   constexpr int CH = D / 4;              // 16-byte pieces per fp32 row
